@@ -1,0 +1,18 @@
+"""Float64 CPU oracle for the attention forward (test infrastructure).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The HIP library never calls it and shares no code
+with it; the two meet only in the seeded inputs of ``workloads``.
+"""
+from .attention_f64 import (  # noqa: F401
+    softmax,
+    online_softmax,
+    attention_naive,
+    attention_naive_rows,
+    attention_dense,
+    attention_dense_rows,
+    attention_varlen,
+    attention_varlen_rows,
+    attention_tiled,
+    scores_to_weights,
+)

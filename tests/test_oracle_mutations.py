@@ -1,0 +1,109 @@
+"""Mutation teeth for the oracle's pins (CPU only).
+
+Each case plants one plausible mistake in the oracle's own source text (a
+dropped term, a wrong sign, index or axis, a transposed operand, a wrong
+log base), loads the mutant as a fresh module, and checks that the pin
+suite rejects it, while the unmodified oracle passes the same suite.
+"""
+import math
+import os
+import types
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+ORACLE_SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                          "oracle", "attention_f64.py")
+
+MUTATIONS = {
+    "drop_scale": ("S = scale * (Q[sel] @ K.T)", "S = (Q[sel] @ K.T)"),
+    "query_as_key": ("S = scale * (Q[sel] @ K.T)", "S = scale * (Q[sel] @ Q.T)"),
+    "no_max_shift": ("P = np.exp(S - m)", "P = np.exp(S)"),
+    "wrong_sign": ("P = np.exp(S - m)", "P = np.exp(m - S)"),
+    "column_normaliser": ("l = P.sum(axis=1, keepdims=True)", "l = P.sum(axis=0, keepdims=True)"),
+    "drop_normaliser": ("O[s:s + sel.size] = (P / l) @ V", "O[s:s + sel.size] = P @ V"),
+    "drop_max_in_L": ("L[s:s + sel.size] = m[:, 0] + np.log(l[:, 0])",
+                      "L[s:s + sel.size] = np.log(l[:, 0])"),
+    "log2_in_L": ("L[s:s + sel.size] = m[:, 0] + np.log(l[:, 0])",
+                  "L[s:s + sel.size] = m[:, 0] + np.log2(l[:, 0])"),
+    "last_key_dropped": ("S = scale * (Q[sel] @ K.T)", "S = scale * (Q[sel] @ K[:-1].T); V = V[:-1]"),
+    "rowmax_over_queries": ("m = S.max(axis=1, keepdims=True)", "m = S.max(axis=0, keepdims=True)"),
+}
+
+
+def load_oracle(mutation=None):
+    src = open(ORACLE_SRC).read()
+    if mutation is not None:
+        old, new = MUTATIONS[mutation]
+        assert src.count(old) == 1, f"mutation site for {mutation!r} not found exactly once"
+        src = src.replace(old, new)
+    mod = types.ModuleType("oracle_under_test")
+    exec(compile(src, ORACLE_SRC, "exec"), mod.__dict__)
+    return mod
+
+
+def _brute(Q, K, V, scale):
+    mpmath.mp.dps = 50
+    n, d = Q.shape
+    m = K.shape[0]
+    O = np.zeros((n, V.shape[1]))
+    L = np.zeros(n)
+    for r in range(n):
+        s = [mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(Q[r, t]) * mpmath.mpf(K[c, t])
+                                             for t in range(d)) for c in range(m)]
+        lse = mpmath.log(mpmath.fsum(mpmath.exp(x) for x in s))
+        L[r] = float(lse)
+        for j in range(V.shape[1]):
+            O[r, j] = float(mpmath.fsum(mpmath.exp(s[c] - lse) * mpmath.mpf(V[c, j])
+                                        for c in range(m)))
+    return O, L
+
+
+def pins_pass(mod) -> bool:
+    """The oracle pin suite in miniature: brute force, a library routine,
+    closed forms and a large-score row. True only if every check holds."""
+    try:
+        with np.errstate(all="ignore"):
+            rng = np.random.default_rng(0)
+            for (n, m, d) in [(3, 5, 4), (4, 4, 2), (1, 3, 3)]:
+                Q = rng.standard_normal((n, d))
+                K = rng.standard_normal((m, d))
+                V = rng.standard_normal((m, d + 1))
+                O, L = mod.attention_naive(Q, K, V, 0.7)
+                Ob, Lb = _brute(Q, K, V, 0.7)
+                if not (np.max(np.abs(O - Ob)) <= 1e-13 and np.max(np.abs(L - Lb)) <= 1e-13):
+                    return False
+            Q = rng.standard_normal((20, 16))
+            K = rng.standard_normal((33, 16))
+            V = rng.standard_normal((33, 16))
+            O, _ = mod.attention_naive(Q, K, V, 0.25)
+            t = lambda a: torch.from_numpy(a)[None, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(t(Q), t(K), t(V), scale=0.25)
+            if not np.max(np.abs(O - ref[0, 0].numpy())) <= 1e-12:
+                return False
+            # identical keys: uniform weights, L = scale q.k + ln m
+            k = rng.standard_normal(16)
+            O, L = mod.attention_naive(Q, np.tile(k, (33, 1)), V, 0.25)
+            if not (np.max(np.abs(O - V.mean(axis=0))) <= 1e-13
+                    and np.max(np.abs(L - (0.25 * Q @ k + math.log(33)))) <= 1e-13):
+                return False
+            # the overflow example: scores 800, 810, 805, 790
+            Qx = np.zeros((1, 4)); Qx[0, 0] = 1.0
+            Kx = np.zeros((4, 4)); Kx[:, 0] = [800.0, 810.0, 805.0, 790.0]
+            O, L = mod.attention_naive(Qx, Kx, np.eye(4), 1.0)
+            if not (np.all(np.isfinite(O)) and abs(O.sum() - 1.0) <= 1e-13):
+                return False
+        return True
+    except Exception:
+        return False
+
+
+def test_unmodified_oracle_passes():
+    assert pins_pass(load_oracle(None))
+
+
+@pytest.mark.parametrize("mutation", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(mutation):
+    assert not pins_pass(load_oracle(mutation))

@@ -1,0 +1,151 @@
+"""Seeded synthetic inputs for the attention forward, shared by the tests,
+the benchmark and the smoke check.
+
+This module holds no attention arithmetic: it only draws random numbers and
+rounds them to the storage dtype. Both the float64 oracle and the HIP path
+receive the same rounded tensors, so their results can be compared element
+by element.
+
+Workloads (sizes and value distributions are those of the five target
+configurations; every draw is seeded, per workload, with
+``numpy.random.default_rng(seed)``):
+
+  single_head_fp32   B=1  H=1  N=256  d=64  fp32  Q,K,V ~ N(0,1)        scale 1/8
+  short_bf16         B=4  H=16 N=1024 d=64  bf16  Q,K,V ~ N(0,1)        scale 1/8
+  long_bf16          B=2  H=32 N=8192 d=128 bf16  Q,K,V ~ N(0,1)        scale 1/sqrt(128)
+  large_logit_fp16   B=16 H=16 N=512  d=64  fp16  Q,K ~ N(0,4^2), V ~ U[-1,1]
+                     scale 1/8 ("a") and 1.0 ("b")
+  varlen_bf16        32 sequences, lengths ~ U{64..4096}, H=16 d=128 bf16,
+                     Q,K,V ~ N(0,1), packed [T,H,d], scale 1/sqrt(128)
+
+Draw order: for varlen the lengths come first, then Q, K, V; for dense
+workloads Q, K, V. Values are drawn as float32 and rounded once to the
+storage dtype with torch (round-to-nearest-even).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+DTYPES = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    dtype: str
+    d: int
+    scale: float
+    B: int = 0
+    H: int = 0
+    N: int = 0
+    # varlen only
+    nseq: int = 0
+    min_len: int = 0
+    max_len: int = 0
+    qk_std: float = 1.0
+    v_uniform: bool = False
+    seed: int = 0
+
+    @property
+    def varlen(self) -> bool:
+        return self.nseq > 0
+
+
+WORKLOADS = {
+    "single_head_fp32": Workload("single_head_fp32", "fp32", 64, 1.0 / 8.0, B=1, H=1, N=256),
+    "short_bf16": Workload("short_bf16", "bf16", 64, 1.0 / 8.0, B=4, H=16, N=1024),
+    "long_bf16": Workload("long_bf16", "bf16", 128, 1.0 / math.sqrt(128.0), B=2, H=32, N=8192),
+    "large_logit_fp16_a": Workload("large_logit_fp16_a", "fp16", 64, 0.125, B=16, H=16, N=512,
+                                   qk_std=4.0, v_uniform=True),
+    "large_logit_fp16_b": Workload("large_logit_fp16_b", "fp16", 64, 1.0, B=16, H=16, N=512,
+                                   qk_std=4.0, v_uniform=True),
+    "varlen_bf16": Workload("varlen_bf16", "bf16", 128, 1.0 / math.sqrt(128.0), H=16,
+                            nseq=32, min_len=64, max_len=4096),
+}
+
+
+def _round(a: np.ndarray, dtype: str) -> torch.Tensor:
+    """float32 numpy -> torch tensor of the storage dtype (RNE), on the CPU."""
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DTYPES[dtype])
+
+
+def draw_qkv(rng: np.random.Generator, shape, dtype: str, qk_std: float = 1.0,
+             v_uniform: bool = False):
+    """Q, K, V of `shape`, drawn in that order from `rng`, rounded to dtype."""
+    q = rng.standard_normal(shape, dtype=np.float32)
+    if qk_std != 1.0:
+        q *= np.float32(qk_std)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    if qk_std != 1.0:
+        k *= np.float32(qk_std)
+    if v_uniform:
+        v = rng.uniform(-1.0, 1.0, size=shape).astype(np.float32)
+    else:
+        v = rng.standard_normal(shape, dtype=np.float32)
+    return _round(q, dtype), _round(k, dtype), _round(v, dtype)
+
+
+def dense_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,
+                 qk_std: float = 1.0, v_uniform: bool = False):
+    """Contiguous [B,H,N,d] Q, K, V (CPU tensors of `dtype`)."""
+    rng = np.random.default_rng(seed)
+    return draw_qkv(rng, (B, H, N, d), dtype, qk_std, v_uniform)
+
+
+def varlen_lengths(nseq: int, lo: int, hi: int, seed: int = 0) -> np.ndarray:
+    """Sequence lengths ~ U{lo..hi} (inclusive), the first draw of the seed."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(lo, hi, endpoint=True, size=nseq).astype(np.int64)
+
+
+def cu_seqlens_of(lengths) -> torch.Tensor:
+    """int32 cumulative offsets [0, n0, n0+n1, ...] (nseq+1 entries)."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    np.cumsum(lengths, out=cu[1:])
+    return torch.from_numpy(cu.astype(np.int32))
+
+
+def varlen_inputs(lengths, H: int, d: int, dtype: str, seed: int = 0,
+                  rng: np.random.Generator | None = None):
+    """Packed [T,H,d] Q, K, V and int32 cu_seqlens for the given lengths.
+
+    When `rng` is None a fresh generator of `seed` is used; the workload
+    generator passes the one that already drew the lengths."""
+    if rng is None:
+        rng = np.random.default_rng(seed)
+    cu = cu_seqlens_of(lengths)
+    T = int(cu[-1])
+    q, k, v = draw_qkv(rng, (T, H, d), dtype)
+    return q, k, v, cu
+
+
+def make(name: str):
+    """Inputs of a named workload.
+
+    Dense: returns dict(q,k,v, B,H,N,d, scale, dtype).
+    Varlen: returns dict(q,k,v, cu_seqlens, lengths, max_seqlen, H,d, scale, dtype).
+    """
+    w = WORKLOADS[name]
+    if w.varlen:
+        rng = np.random.default_rng(w.seed)
+        lengths = rng.integers(w.min_len, w.max_len, endpoint=True, size=w.nseq).astype(np.int64)
+        q, k, v, cu = varlen_inputs(lengths, w.H, w.d, w.dtype, rng=rng)
+        return dict(q=q, k=k, v=v, cu_seqlens=cu, lengths=lengths,
+                    max_seqlen=int(lengths.max()), H=w.H, d=w.d, scale=w.scale,
+                    dtype=w.dtype)
+    q, k, v = dense_inputs(w.B, w.H, w.N, w.d, w.dtype, w.seed, w.qk_std, w.v_uniform)
+    return dict(q=q, k=k, v=v, B=w.B, H=w.H, N=w.N, d=w.d, scale=w.scale, dtype=w.dtype)
+
+
+def attention_flops(B: int, H: int, N: int, d: int) -> int:
+    """Counted work of one forward: two N x N x d products per head, 2 flops per MAC."""
+    return 4 * B * H * N * N * d
+
+
+def varlen_flops(lengths, H: int, d: int) -> int:
+    return 4 * H * d * int(sum(int(n) * int(n) for n in lengths))
