@@ -1,0 +1,159 @@
+"""MI355X (gfx950) FlashAttention-2 forward: thin Python binding of libfa.so.
+
+The C ABI (include/fa.h) is the product; this module only marshals
+arguments. Every step of the forward runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.
+
+    fa_fwd(Q, K, V, O, L, B, H, N, d, scale, dtype, stream)        -> None
+    fa_fwd_varlen(Q, K, V, O, L, cu_seqlens, nseq, total_tokens,
+                  max_seqlen, H, d, scale, dtype, stream)           -> None
+    fa_strerror(status) -> str,  fa_version() -> int
+
+take raw integers (device addresses, sizes, the stream handle) exactly as
+the C functions do and raise ``FaError`` on a non-zero status.
+
+    forward(q, k, v, scale=None)                    -> (o, lse)
+    forward_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None) -> (o, lse)
+
+take torch tensors on a GPU, allocate the outputs with torch.empty and call
+the entry points above on the current stream.
+
+If libfa.so is missing or cannot be loaded, every call raises: there is no
+fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FA_F32", "FA_F16", "FA_BF16", "FaError", "LIB_PATH", "load", "fa_fwd", "fa_fwd_varlen",
+    "fa_strerror", "fa_version", "forward", "forward_varlen", "EXPORTED_SYMBOLS",
+]
+
+FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+STATUS = {
+    0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_HEADDIM", -4: "FA_ERR_DTYPE",
+    -5: "FA_ERR_ALIGN", -6: "FA_ERR_ALIAS", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_SCALE",
+    -9: "FA_ERR_SIZE",
+}
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_strerror", "fa_version")
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+        self.name = STATUS.get(status, "unknown")
+
+
+def load() -> ctypes.CDLL:
+    """Load libfa.so once and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_attention_26_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
+    lib.fa_fwd.restype = i32
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.fa_fwd_varlen.restype = i32
+    lib.fa_strerror.argtypes = [i32]
+    lib.fa_strerror.restype = ctypes.c_char_p
+    lib.fa_version.argtypes = []
+    lib.fa_version.restype = i32
+    _lib = lib
+    return lib
+
+
+def fa_strerror(status: int) -> str:
+    return load().fa_strerror(int(status)).decode()
+
+
+def fa_version() -> int:
+    return int(load().fa_version())
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise FaError(status, fa_strerror(status))
+
+
+def fa_fwd(Q, K, V, O, L, B, H, N, d, scale, dtype, stream) -> None:
+    _check(load().fa_fwd(Q, K, V, O, L, int(B), int(H), int(N), int(d), float(scale), int(dtype),
+                         stream))
+
+
+def fa_fwd_varlen(Q, K, V, O, L, cu_seqlens, nseq, total_tokens, max_seqlen, H, d, scale, dtype,
+                  stream) -> None:
+    _check(load().fa_fwd_varlen(Q, K, V, O, L, cu_seqlens, int(nseq), int(total_tokens),
+                                int(max_seqlen), int(H), int(d), float(scale), int(dtype), stream))
+
+
+# ---------------------------------------------------------------------------
+# torch conveniences (argument marshalling only)
+# ---------------------------------------------------------------------------
+def _dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: FA_F32, torch.float16: FA_F16, torch.bfloat16: FA_BF16}
+    if t.dtype not in codes:
+        raise TypeError(f"unsupported dtype {t.dtype}; expected float32, float16 or bfloat16")
+    return codes[t.dtype]
+
+
+def _stream_handle(device) -> int:
+    import torch
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _require(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def forward(q, k, v, scale: float | None = None, out=None, lse=None):
+    """Dense forward on contiguous [B, H, N, d] tensors; returns (o, lse[B,H,N] fp32)."""
+    import torch
+    _require(q.dim() == 4 and q.shape == k.shape == v.shape, "q, k, v must share shape [B,H,N,d]")
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    _require(q.is_cuda and k.is_cuda and v.is_cuda, "q, k, v must be GPU tensors")
+    _require(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(),
+             "q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    L = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), L.data_ptr(), B, H, N, d,
+           scale, _dtype_code(q), _stream_handle(q.device))
+    return o, L
+
+
+def forward_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: float | None = None, out=None,
+                   lse=None):
+    """Packed forward on contiguous [T, H, d] tensors with int32 cu_seqlens[nseq+1]
+    on the same device; returns (o, lse[H,T] fp32)."""
+    import torch
+    _require(q.dim() == 3 and q.shape == k.shape == v.shape, "q, k, v must share shape [T,H,d]")
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    _require(q.is_cuda and cu_seqlens.is_cuda, "q, k, v, cu_seqlens must be GPU tensors")
+    _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1,
+             "cu_seqlens must be a 1-D int32 tensor")
+    _require(q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
+             and cu_seqlens.is_contiguous(), "inputs must be contiguous")
+    T, H, d = q.shape
+    nseq = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    L = torch.empty((H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), L.data_ptr(),
+                  cu_seqlens.data_ptr(), nseq, T, int(max_seqlen), H, d, scale, _dtype_code(q),
+                  _stream_handle(q.device))
+    return o, L

@@ -1,0 +1,161 @@
+// C-ABI entry points of the FlashAttention-2 forward library (include/fa.h):
+// argument validation, work-grid sizing and dispatch to the gfx950 kernels.
+//
+// Validation touches no HIP API, so every error path returns before
+// anything is enqueued (and can be exercised without a GPU).
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_common.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Half-open byte ranges [a, a+na) and [b, b+nb) intersect.
+bool overlap(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return na > 0 && nb > 0 && x < y + nb && y < x + na;
+}
+
+int elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
+
+bool valid_dtype(int dtype) { return dtype == FA_F32 || dtype == FA_F16 || dtype == FA_BF16; }
+
+int rows_per_block(int dtype) {
+  return dtype == FA_F32 ? fa::kRowsPerBlockF32 : fa::kRowsPerBlock16;
+}
+
+// Shared checks on the dense and varlen entry points after the sizes are
+// known to be non-negative and non-empty.
+int check_buffers(const void* Q, const void* K, const void* V, const void* O, const float* L,
+                  uint64_t qkvo_bytes, uint64_t l_bytes) {
+  if (!Q || !K || !V || !O || !L) return FA_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(L))
+    return FA_ERR_ALIGN;
+  if (overlap(O, qkvo_bytes, Q, qkvo_bytes) || overlap(O, qkvo_bytes, K, qkvo_bytes) ||
+      overlap(O, qkvo_bytes, V, qkvo_bytes) || overlap(L, l_bytes, Q, qkvo_bytes) ||
+      overlap(L, l_bytes, K, qkvo_bytes) || overlap(L, l_bytes, V, qkvo_bytes) ||
+      overlap(L, l_bytes, O, qkvo_bytes))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+int launch(const fa::FwdParams& p, int d, int dtype, bool varlen, void* stream) {
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (dtype == FA_F32)
+    e = fa::launch_fwd_f32(p, d, varlen, s);
+  else
+    e = fa::launch_fwd_mfma16(p, d, dtype == FA_BF16, varlen, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+// Workgroups are 256 threads; keep the grid within 32-bit thread counts.
+constexpr int64_t kMaxBlocks = (int64_t{1} << 32) / 256 - 1;
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H, int N,
+           int d, float scale, int dtype, void* stream) {
+  if (!valid_dtype(dtype)) return FA_ERR_DTYPE;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+
+  if ((int64_t)N * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
+  const int br = rows_per_block(dtype);
+  if ((int64_t)((N + br - 1) / br) * H * B > kMaxBlocks) return FA_ERR_SIZE;
+  const uint64_t elems = (uint64_t)B * H * N * d;
+  const int st = check_buffers(Q, K, V, O, L, elems * elem_bytes(dtype), (uint64_t)B * H * N * 4);
+  if (st != FA_OK) return st;
+
+  fa::FwdParams p{};
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.lse = L;
+  p.cu_seqlens = nullptr;
+  p.batch_stride = (int64_t)H * N * d;
+  p.head_stride = (int64_t)N * d;
+  p.row_stride = d;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.total_tokens = 0;
+  p.q_blocks = (N + br - 1) / br;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return launch(p, d, dtype, false, stream);
+}
+
+int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L,
+                  const int32_t* cu_seqlens, int nseq, int total_tokens, int max_seqlen, int H,
+                  int d, float scale, int dtype, void* stream) {
+  if (!valid_dtype(dtype)) return FA_ERR_DTYPE;
+  if (nseq < 0 || total_tokens < 0 || max_seqlen < 0 || H < 0) return FA_ERR_SHAPE;
+  if (max_seqlen > total_tokens) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (nseq == 0 || total_tokens == 0 || max_seqlen == 0 || H == 0) return FA_OK;
+
+  if ((int64_t)max_seqlen * H * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
+  const int br = rows_per_block(dtype);
+  if ((int64_t)((max_seqlen + br - 1) / br) * H * nseq > kMaxBlocks) return FA_ERR_SIZE;
+  if (!cu_seqlens) return FA_ERR_NULL;
+  const uint64_t elems = (uint64_t)total_tokens * H * d;
+  const int st =
+      check_buffers(Q, K, V, O, L, elems * elem_bytes(dtype), (uint64_t)H * total_tokens * 4);
+  if (st != FA_OK) return st;
+  if ((reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) != 0) return FA_ERR_ALIGN;
+  const uint64_t cu_bytes = (uint64_t)(nseq + 1) * 4;
+  if (overlap(O, elems * elem_bytes(dtype), cu_seqlens, cu_bytes) ||
+      overlap(L, (uint64_t)H * total_tokens * 4, cu_seqlens, cu_bytes))
+    return FA_ERR_ALIAS;
+
+  fa::FwdParams p{};
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.lse = L;
+  p.cu_seqlens = cu_seqlens;
+  p.batch_stride = 0;
+  p.head_stride = d;
+  p.row_stride = H * d;
+  p.B = nseq;
+  p.H = H;
+  p.N = max_seqlen;
+  p.total_tokens = total_tokens;
+  p.q_blocks = (max_seqlen + br - 1) / br;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return launch(p, d, dtype, true, stream);
+}
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative or inconsistent sizes";
+    case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension must be 64 or 128";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype must be FA_F32, FA_F16 or FA_BF16";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not suitably aligned";
+    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or the other output";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime refused the kernel launch";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
+    case FA_ERR_SIZE: return "FA_ERR_SIZE: tensor too large for 32-bit in-head offsets";
+    default: return "unknown fa_status";
+  }
+}
+
+int fa_version(void) { return kVersion; }
+
+}  // extern "C"

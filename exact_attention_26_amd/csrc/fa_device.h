@@ -1,0 +1,63 @@
+// Device-side helpers shared by the forward kernels: workgroup -> work-unit
+// mapping and small vector types.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fa_common.h"
+
+namespace fa {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+
+// The chip has 8 XCDs, each with its own L2, and consecutive workgroup ids
+// are dealt to the XCDs round-robin. Work units that share K/V (the
+// Q-blocks of one head) get consecutive logical ids, so this mapping sends
+// a contiguous run of logical ids to one XCD: workgroup w runs logical unit
+// (w % 8) * (G / 8) + w / 8. Ids past the last multiple of 8 map to
+// themselves, so the mapping is a bijection of [0, G).
+__device__ __forceinline__ int xcd_remap(int w, int G) {
+  const int per = G >> 3;
+  const int full = per << 3;
+  return (w < full) ? ((w & 7) * per + (w >> 3)) : w;
+}
+
+// One work unit: `rows_per_block` query rows of one (batch or sequence, head).
+struct WorkUnit {
+  int n;             // keys (= queries) of this sequence/head
+  int q0;            // first query row of the unit
+  int64_t base;      // element offset of row 0 of this head in Q/K/V/O
+  int64_t lse_base;  // element offset of row 0 of this head in L
+};
+
+// Logical id order: head-major (all Q-blocks of a head are consecutive).
+// Returns false when the unit lies past the end of its sequence (varlen).
+template <bool VARLEN>
+__device__ __forceinline__ bool resolve_unit(const FwdParams& p, int rows_per_block,
+                                             WorkUnit& u) {
+  const int id = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int qb = id % p.q_blocks;
+  const int rest = id / p.q_blocks;
+  const int h = rest % p.H;
+  const int b = rest / p.H;
+  u.q0 = qb * rows_per_block;
+  if (VARLEN) {
+    const int start = p.cu_seqlens[b];
+    u.n = p.cu_seqlens[b + 1] - start;
+    u.base = (int64_t)start * p.row_stride + (int64_t)h * p.head_stride;
+    u.lse_base = (int64_t)h * p.total_tokens + start;
+  } else {
+    u.n = p.N;
+    u.base = (int64_t)b * p.batch_stride + (int64_t)h * p.head_stride;
+    u.lse_base = ((int64_t)b * p.H + h) * p.N;
+  }
+  return u.q0 < u.n;
+}
+
+}  // namespace fa

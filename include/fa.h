@@ -1,0 +1,110 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 forward library.
+ *
+ * What is computed. For every (batch, head) -- or every (sequence, head)
+ * in the packed variable-length entry -- and every query row r:
+ *
+ *     S[r, c] = scale * dot(Q[r, :], K[c, :])         over all keys c
+ *     O[r, :] = sum_c softmax(S[r, :])[c] * V[c, :]
+ *     L[r]    = max_c S[r, c] + ln( sum_c exp(S[r, c] - max_c S[r, c]) )
+ *
+ * i.e. the forward pass of "Kernel visualization: Flash Attention 2"
+ * (tinyvolt.com): its fa2 kernel takes Q, K, V and writes O and the single
+ * array L = m + log(l) (sections "Steps" and "Write the data back to HBM"),
+ * with the score scale applied to the dot product (section "Iteration
+ * j = 0"). It is the same function as plain softmax attention, not an
+ * approximation ("FlashAttention -- for programmers, not researchers",
+ * STAGE 4 and DEMO 6). No causal mask, no dropout, no bias; query and
+ * key/value head counts are equal.
+ *
+ * Conventions shared by every entry point:
+ *   - Q, K, V, O, L and cu_seqlens are DEVICE pointers, allocated and owned
+ *     by the caller. The library allocates nothing, keeps no per-call state
+ *     and never synchronises: work is enqueued on `stream` (a hipStream_t
+ *     passed as void*; NULL = the default stream) and the caller
+ *     synchronises. Calls on one stream run in order.
+ *   - Storage dtype of Q, K, V and O is `dtype` (fa_dtype). Arithmetic:
+ *     products of dtype values summed in fp32; softmax statistics m, l in
+ *     fp32; for fp16/bf16 the probabilities are rounded to dtype (round to
+ *     nearest even) as operands of the P.V product; O is rounded to dtype
+ *     once, after the single division by l. L is always fp32, natural log.
+ *   - Head dimension d is 64 or 128 (FA_ERR_HEADDIM otherwise).
+ *   - `scale` must be finite and > 0 (FA_ERR_SCALE otherwise).
+ *   - Every pointer must be 16-byte aligned (FA_ERR_ALIGN).
+ *   - O and L must not overlap Q, K, V or each other (FA_ERR_ALIAS).
+ *   - Empty problems (a zero size) return FA_OK without launching.
+ *   - Errors are returned, never raised or printed; nothing is enqueued
+ *     when a check fails. A kernel launch error is FA_ERR_LAUNCH.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_F32 = 0,
+  FA_F16 = 1,
+  FA_BF16 = 2
+} fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,     /* a required pointer is NULL                        */
+  FA_ERR_SHAPE = -2,    /* a negative size, or inconsistent varlen sizes     */
+  FA_ERR_HEADDIM = -3,  /* d not in {64, 128}                                */
+  FA_ERR_DTYPE = -4,    /* dtype not an fa_dtype value                       */
+  FA_ERR_ALIGN = -5,    /* a pointer not 16-byte aligned                     */
+  FA_ERR_ALIAS = -6,    /* an output overlaps an input or the other output   */
+  FA_ERR_LAUNCH = -7,   /* the HIP runtime refused the kernel launch         */
+  FA_ERR_SCALE = -8,    /* scale not finite or not > 0                       */
+  FA_ERR_SIZE = -9      /* a tensor too large for 32-bit in-head offsets     */
+} fa_status;
+
+/*
+ * Dense forward.
+ *   Q, K, V, O : contiguous [B, H, N, d] tensors of `dtype`
+ *                (element (b,h,n,k) at ((b*H + h)*N + n)*d + k).
+ *   L          : contiguous [B, H, N] float32 (natural-log logsumexp).
+ *   B, H, N    : >= 0; N*d must be below 2^31.
+ * The [KV] kernel signature fa2(Q, K, V, O, L, N, scale) with its per-head
+ * offsets bh*N*D and bh*N ("Steps"), widened by batch, heads, d and dtype.
+ * Returns an fa_status.
+ */
+int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
+           int B, int H, int N, int d, float scale, int dtype, void* stream);
+
+/*
+ * Packed variable-length forward (self-attention within each sequence).
+ *   Q, K, V, O   : contiguous [T, H, d] tensors of `dtype`; token t of
+ *                  head h at (t*H + h)*d. Sequence s owns tokens
+ *                  cu_seqlens[s] .. cu_seqlens[s+1]-1 and attends to those
+ *                  tokens only (no causal mask).
+ *   L            : contiguous [H, T] float32; L[h*T + t].
+ *   cu_seqlens   : device int32[nseq + 1], cu_seqlens[0] = 0, non-decreasing,
+ *                  cu_seqlens[nseq] = total_tokens = T. Its contents are the
+ *                  caller's responsibility: they are read on the device and
+ *                  not checked.
+ *   max_seqlen   : host-side upper bound of every sequence length; it sizes
+ *                  the grid. Rows of a longer sequence beyond max_seqlen are
+ *                  not written. max_seqlen*H*d must be below 2^31.
+ * Returns an fa_status.
+ */
+int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L,
+                  const int32_t* cu_seqlens, int nseq, int total_tokens, int max_seqlen,
+                  int H, int d, float scale, int dtype, void* stream);
+
+/* Static, NUL-terminated description of an fa_status value. */
+const char* fa_strerror(int status);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */
