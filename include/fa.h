@@ -30,7 +30,8 @@
  *     once, after the single division by l. L is always fp32, natural log.
  *   - Head dimension d is 64 or 128 (FA_ERR_HEADDIM otherwise).
  *   - `scale` must be finite and > 0 (FA_ERR_SCALE otherwise).
- *   - Every pointer must be 16-byte aligned (FA_ERR_ALIGN).
+ *   - Q, K, V, O and L must be 16-byte aligned, cu_seqlens 4-byte aligned
+ *     (FA_ERR_ALIGN).
  *   - O and L must not overlap Q, K, V or each other (FA_ERR_ALIAS).
  *   - Empty problems (a zero size) return FA_OK without launching.
  *   - Errors are returned, never raised or printed; nothing is enqueued
