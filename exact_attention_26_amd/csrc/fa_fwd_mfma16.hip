@@ -27,7 +27,22 @@
 //    j is computed, then written to the other stage; one barrier per tile.
 //  * O (fp32) lives in MFMA accumulators for the whole loop, one query per
 //    lane, so the rescale by alpha is a per-lane scalar multiply.
+#include <type_traits>
+
 #include "fa_device.h"
+
+// Optionally raise the wave priority around MFMA bursts (s_setprio). Off by
+// default: with two waves per SIMD it measured no faster on MI355X.
+#ifndef FA_SETPRIO
+#define FA_SETPRIO 0
+#endif
+#if FA_SETPRIO
+#define FA_PRIO_HI() __builtin_amdgcn_s_setprio(1)
+#define FA_PRIO_LO() __builtin_amdgcn_s_setprio(0)
+#else
+#define FA_PRIO_HI()
+#define FA_PRIO_LO()
+#endif
 
 namespace fa {
 namespace {
@@ -128,46 +143,56 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
     qf[s] = __builtin_bit_cast(vec8, w);
   }
 
-  // Tile fetch assignments.
+  // Tile fetch assignments. K: 16-byte chunks, row-major. V: each thread
+  // owns 4 consecutive keys x VC columns, which it writes transposed.
   constexpr int CPR = D / 8;                 // 16-byte chunks per K row
   constexpr int KCH = BC * CPR / kThreads;   // K chunks per thread
-  constexpr int VC = D / 16;                 // V columns per thread (4 keys each)
+  constexpr int VC = D / 16;                 // V columns per thread
   using vchunk = typename VChunk<VC>::type;
-  const int vcg = tid & 15;   // V column group
-  const int vkg = tid >> 4;   // V key group: keys 4*vkg .. 4*vkg+3
+  // The 16 lanes that share an LDS write pass hold the 16 key groups of one
+  // column group, so each transposed ds_write_b64 pass fills one 128-byte
+  // V^T row segment: no bank conflicts.
+  const int vkg = tid & 15;   // V key group: keys 4*vkg .. 4*vkg+3
+  const int vcg = tid >> 4;   // V column group
   // Position of key 4*vkg in the permuted V^T row: key 16t+8h+4q+r is stored
   // at 16t+8q+4h+r, so lane group q of a P.V MFMA reads 8 contiguous keys.
   const int vpos = ((4 * vkg) & ~15) | (((4 * vkg) & 4) << 1) | (((4 * vkg) & 8) >> 1);
+  int krow[KCH], kcol[KCH];
+#pragma unroll
+  for (int r = 0; r < KCH; ++r) {
+    krow[r] = (tid + kThreads * r) / CPR;
+    kcol[r] = ((tid + kThreads * r) % CPR) * 8;
+  }
 
   u32x4 kr[KCH];
   vchunk vr[4];
 
-  auto fetch = [&](int kb) {
+  // Global -> registers for the tile starting at key kb. In the ragged last
+  // tile (tail) rows past the end are clamped to row n-1: the loads stay in
+  // bounds and those keys are masked out of the scores.
+  auto fetch = [&](int kb, bool tail) {
+    const unsigned short* Kt = Kg + (int64_t)kb * rs;
+    const unsigned short* Vt = Vg + (int64_t)kb * rs;
+    if (!tail) {
 #pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int c = tid + kThreads * r;
-      const int key = kb + c / CPR;
-      const int col = (c % CPR) * 8;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (key < n) w = *(const u32x4*)(Kg + key * rs + col);
-      kr[r] = w;
-    }
+      for (int r = 0; r < KCH; ++r) kr[r] = *(const u32x4*)(Kt + (krow[r] * rs + kcol[r]));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = kb + 4 * vkg + r;
-      vchunk w = {};
-      if (key < n) w = *(const vchunk*)(Vg + key * rs + vcg * VC);
-      vr[r] = w;
+      for (int r = 0; r < 4; ++r) vr[r] = *(const vchunk*)(Vt + ((4 * vkg + r) * rs + vcg * VC));
+    } else {
+      const int last = n - 1 - kb;
+#pragma unroll
+      for (int r = 0; r < KCH; ++r)
+        kr[r] = *(const u32x4*)(Kt + (min(krow[r], last) * rs + kcol[r]));
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vr[r] = *(const vchunk*)(Vt + (min(4 * vkg + r, last) * rs + vcg * VC));
     }
   };
   auto stash = [&](int stage) {
     unsigned short* Ks = lds + stage * STAGE;
     unsigned short* Vs = Ks + KT;
 #pragma unroll
-    for (int r = 0; r < KCH; ++r) {
-      const int c = tid + kThreads * r;
-      *(u32x4*)(Ks + (c / CPR) * KSTR + (c % CPR) * 8) = kr[r];
-    }
+    for (int r = 0; r < KCH; ++r) *(u32x4*)(Ks + krow[r] * KSTR + kcol[r]) = kr[r];
 #pragma unroll
     for (int c = 0; c < VC; ++c) {
       u32x2 w;
@@ -186,34 +211,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
   float l = 0.f;        // running sum of this lane's half of the keys
   const float c2 = p.scale_log2;
 
-  const int tiles = (n + BC - 1) / BC;
-  fetch(0);
-  stash(0);
-  __syncthreads();
-
-  for (int j = 0; j < tiles; ++j) {
-    const int kb = j * BC;
-    const bool more = (j + 1) < tiles;
-    if (more) fetch(kb + BC);
-
-    const unsigned short* Ks = lds + (j & 1) * STAGE;
+  // One key tile: scores, online softmax update, P.V. MASKED marks the
+  // ragged last tile (keys >= n get probability 0).
+  auto step = [&](auto masked, int stage, int kb) {
+    constexpr bool MASKED = decltype(masked)::value;
+    const unsigned short* Ks = lds + stage * STAGE;
     const unsigned short* Vs = Ks + KT;
 
     // S^T tile: two 32-key MFMA tiles; lane holds query l32, keys
     // kt*32 + 8*(i/4) + 4*g + (i%4) in register i.
     f32x16 s[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
+    FA_PRIO_HI();
 #pragma unroll
-      for (int ss = 0; ss < D / 16; ++ss) {
+    for (int ss = 0; ss < D / 16; ++ss)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
         const vec8 a = *(const vec8*)(Ks + (kt * 32 + l32) * KSTR + 16 * ss + 8 * g);
         s[kt] = mfma32x32x16<BF16>(a, qf[ss], s[kt]);
       }
-    }
+    FA_PRIO_LO();
 
-    if (kb + BC > n) {  // ragged last tile: keys >= n get score -inf (p = 0)
+    if constexpr (MASKED) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -223,52 +245,76 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
         }
     }
 
-    // Online softmax update for this lane's query.
-    float mx = s[0][0];
+    // Row max: four independent max3 chains, then one exchange with lane ^ 32.
+    float mq[4];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kt][i]);
+    for (int q = 0; q < 4; ++q) {
+      const f32x16& a = s[q >> 1];
+      const int b = 8 * (q & 1);
+      mq[q] = fmaxf(fmaxf(fmaxf(a[b + 0], a[b + 1]), fmaxf(a[b + 2], a[b + 3])),
+                    fmaxf(fmaxf(a[b + 4], a[b + 5]), fmaxf(a[b + 6], a[b + 7])));
+    }
+    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mnew = fmaxf(m, mx);
-    const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c2);
+    const bool grew = mnew > m;
+    const float alpha = grew ? __builtin_amdgcn_exp2f((m - mnew) * c2) : 1.f;
     const float mc = mnew * c2;
-    float rsum = 0.f;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const float e = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -mc));
         s[kt][i] = e;
-        rsum += e;
+        ls[i & 3] += e;
       }
-    l = l * alpha + rsum;
+    l = l * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
     m = mnew;
+    // Rescale the running output only if some lane's max moved (alpha != 1).
+    if (__any(grew)) {
 #pragma unroll
-    for (int t = 0; t < D / 32; ++t)
+      for (int t = 0; t < D / 32; ++t)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+    }
 
     // O^T += V^T P^T over the 64 keys, 16 keys per MFMA. Slot jj of lane
     // group g in MFMA t is key 16t + 8*(jj/4) + 4g + jj%4, which is S^T
     // register 8*(t%2) + jj of key tile t/2.
+    vec8 pb[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       u32x4 pw;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         pw[q] = pack2<BF16>(s[t >> 1][8 * (t & 1) + 2 * q], s[t >> 1][8 * (t & 1) + 2 * q + 1]);
-      const vec8 pb = __builtin_bit_cast(vec8, pw);
+      pb[t] = __builtin_bit_cast(vec8, pw);
+    }
+    FA_PRIO_HI();
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const vec8 a = *(const vec8*)(Vs + (dt * 32 + l32) * VSTR + 16 * t + 8 * g);
-        o[dt] = mfma32x32x16<BF16>(a, pb, o[dt]);
+        o[dt] = mfma32x32x16<BF16>(a, pb[t], o[dt]);
       }
-    }
+    FA_PRIO_LO();
+  };
 
+  const int nfull = n / BC;                  // tiles with all BC keys valid
+  const int tiles = (n + BC - 1) / BC;
+  fetch(0, nfull == 0);
+  stash(0);
+  __syncthreads();
+  for (int j = 0; j < nfull; ++j) {
+    const bool more = (j + 1) < tiles;
+    if (more) fetch((j + 1) * BC, j + 1 == nfull);
+    step(std::false_type{}, j & 1, j * BC);
     if (more) stash((j + 1) & 1);
     __syncthreads();
   }
+  if (nfull < tiles) step(std::true_type{}, nfull & 1, nfull * BC);
 
   // Write-back: divide once by l, L = m*scale + ln l.
   l += __shfl_xor(l, 32);
