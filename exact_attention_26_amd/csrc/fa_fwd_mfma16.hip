@@ -19,35 +19,31 @@
 //  * P = exp2(S*c - m*c) (c = scale*log2 e) is rounded to the storage dtype
 //    and fed from the S^T accumulator registers straight into the P.V
 //    MFMA as its B operand (O^T = V^T P^T): no LDS round trip for P.
-//  * K tiles sit in LDS row-major (row padded by 16 bytes against bank
-//    conflicts); V tiles are written to LDS transposed, V^T[d][key], with
-//    the keys of each 16-key group permuted so that the 8 keys one lane
-//    needs for a P.V MFMA are contiguous (one 16-byte LDS read).
-//  * Two LDS stages: tile j+1 is fetched from HBM into registers while tile
-//    j is computed, then written to the other stage; one barrier per tile.
+//  * K and V tiles travel HBM -> LDS with global_load_lds_dwordx4 (no
+//    staging registers, no LDS write instructions). Both stay row-major in
+//    LDS with an XOR swizzle of their columns:
+//      K: 16-byte chunk c of row r sits at chunk c ^ kswz(r); a lane reads
+//         one 16-byte chunk of one key row per S^T MFMA (ds_read_b128);
+//      V: 64-byte chunk c of row r sits at chunk c ^ vswz(r); the P.V
+//         operand (8 keys of one d column per lane) is read with the gfx950
+//         transposing load ds_read_b64_tr_b16: within each 16-lane block,
+//         lane l receives element l%4 of the 4-element vectors loaded by
+//         lanes l/4, l/4+4, l/4+8 and l/4+12.
+//    Both read patterns are free of LDS bank conflicts.
+//  * Two LDS stages: tile j+1 streams into one stage while tile j is
+//    computed from the other; one barrier per tile.
 //  * O (fp32) lives in MFMA accumulators for the whole loop, one query per
-//    lane, so the rescale by alpha is a per-lane scalar multiply.
+//    lane, so the rescale by alpha is a per-lane scalar multiply, skipped
+//    when no lane's running max moved.
 #include <type_traits>
 
 #include "fa_device.h"
-
-// Optionally raise the wave priority around MFMA bursts (s_setprio). Off by
-// default: with two waves per SIMD it measured no faster on MI355X.
-#ifndef FA_SETPRIO
-#define FA_SETPRIO 0
-#endif
-#if FA_SETPRIO
-#define FA_PRIO_HI() __builtin_amdgcn_s_setprio(1)
-#define FA_PRIO_LO() __builtin_amdgcn_s_setprio(0)
-#else
-#define FA_PRIO_HI()
-#define FA_PRIO_LO()
-#endif
 
 namespace fa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
 constexpr int BR = kRowsPerBlock16;  // query rows per workgroup (32 per wave)
 constexpr int BC = 64;               // keys per tile
 
@@ -61,6 +57,12 @@ template <>
 struct Elem<false> {
   using vec8 = f16x8;
 };
+
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 template <bool BF16>
 __device__ __forceinline__ f32x16 mfma32x32x16(typename Elem<BF16>::vec8 a,
@@ -90,39 +92,33 @@ __device__ __forceinline__ unsigned pack2(float a, float b) {
   }
 }
 
-template <int C>
-struct VChunk;
-template <>
-struct VChunk<8> {
-  using type = u32x4;
+// LDS tile geometry for head dimension D (16-bit elements).
+template <int D>
+struct Tile {
+  static constexpr int ROWB = D * 2;                 // bytes per key row
+  static constexpr int TILEB = BC * ROWB;            // bytes per K (or V) tile
+  static constexpr int STAGEB = 2 * TILEB;           // K tile + V tile
+  static constexpr int ROWS_PER_256 = 256 / ROWB;    // rows sharing one 256-byte bank sweep
+  static constexpr int KCHUNKS = ROWB / 16;          // 16-byte chunks per row
+  static constexpr int VCHUNKS = ROWB / 64;          // 64-byte chunks per row
+  static constexpr int DMA_PER_WAVE = TILEB / 1024 / kWaves;  // 1 KiB copies per wave
+  // Rows read together get distinct chunk positions, hence distinct banks.
+  __device__ static int kswz(int r) { return (r / ROWS_PER_256) & (KCHUNKS - 1); }
+  __device__ static int vswz(int r) { return (r / ROWS_PER_256) & (VCHUNKS - 1); }
 };
-template <>
-struct VChunk<4> {
-  using type = u32x2;
-};
-
-template <typename T>
-__device__ __forceinline__ unsigned half16(const T& v, int c) {
-  const unsigned w = v[c >> 1];
-  return (c & 1) ? (w >> 16) : (w & 0xffffu);
-}
 
 template <bool BF16, int D, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
   using vec8 = typename Elem<BF16>::vec8;
-  constexpr int KSTR = D + 8;   // 16-bit elements per K row in LDS
-  constexpr int VSTR = BC + 8;  // 16-bit elements per V^T row in LDS
-  constexpr int KT = BC * KSTR;
-  constexpr int VT = D * VSTR;
-  constexpr int STAGE = KT + VT;
-  __shared__ __attribute__((aligned(16))) unsigned short lds[2 * STAGE];
+  using T = Tile<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * T::STAGEB];
 
   WorkUnit u;
   if (!resolve_unit<VARLEN>(p, BR, u)) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int g = lane >> 5;
   const int n = u.n;
@@ -143,64 +139,50 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
     qf[s] = __builtin_bit_cast(vec8, w);
   }
 
-  // Tile fetch assignments. K: 16-byte chunks, row-major. V: each thread
-  // owns 4 consecutive keys x VC columns, which it writes transposed.
-  constexpr int CPR = D / 8;                 // 16-byte chunks per K row
-  constexpr int KCH = BC * CPR / kThreads;   // K chunks per thread
-  constexpr int VC = D / 16;                 // V columns per thread
-  using vchunk = typename VChunk<VC>::type;
-  // The 16 lanes that share an LDS write pass hold the 16 key groups of one
-  // column group, so each transposed ds_write_b64 pass fills one 128-byte
-  // V^T row segment: no bank conflicts.
-  const int vkg = tid & 15;   // V key group: keys 4*vkg .. 4*vkg+3
-  const int vcg = tid >> 4;   // V column group
-  // Position of key 4*vkg in the permuted V^T row: key 16t+8h+4q+r is stored
-  // at 16t+8q+4h+r, so lane group q of a P.V MFMA reads 8 contiguous keys.
-  const int vpos = ((4 * vkg) & ~15) | (((4 * vkg) & 4) << 1) | (((4 * vkg) & 8) >> 1);
-  int krow[KCH], kcol[KCH];
+  // Direct-to-LDS copies. Copy r of this wave fills bytes
+  // [1024*(wave*NDMA + r), +1024) of the K (and of the V) tile; lane i
+  // writes 16 bytes at +16*i, i.e. 16-byte slot s of the tile. Slot s is
+  // (row, stored chunk); the lane fetches the logical chunk the swizzle
+  // stores there.
+  constexpr int NDMA = T::DMA_PER_WAVE;
+  int drow[NDMA], kcol[NDMA], vcol[NDMA];
 #pragma unroll
-  for (int r = 0; r < KCH; ++r) {
-    krow[r] = (tid + kThreads * r) / CPR;
-    kcol[r] = ((tid + kThreads * r) % CPR) * 8;
+  for (int r = 0; r < NDMA; ++r) {
+    const int s = (wave * NDMA + r) * 64 + lane;
+    const int row = s / T::KCHUNKS;
+    const int pos = s % T::KCHUNKS;
+    drow[r] = row;
+    kcol[r] = (pos ^ T::kswz(row)) * 8;
+    vcol[r] = ((((pos >> 2) ^ T::vswz(row)) << 2) | (pos & 3)) * 8;
   }
-
-  u32x4 kr[KCH];
-  vchunk vr[4];
-
-  // Global -> registers for the tile starting at key kb. In the ragged last
-  // tile (tail) rows past the end are clamped to row n-1: the loads stay in
-  // bounds and those keys are masked out of the scores.
-  auto fetch = [&](int kb, bool tail) {
+  // Tile at key kb into LDS stage `stage`. In the ragged last tile (tail)
+  // rows past the end are clamped to row n-1: loads stay in bounds and those
+  // keys are masked out of the scores.
+  auto fetch = [&](int stage, int kb, bool tail) {
     const unsigned short* Kt = Kg + (int64_t)kb * rs;
     const unsigned short* Vt = Vg + (int64_t)kb * rs;
-    if (!tail) {
+    lds_u8* base = (lds_u8*)lds + stage * T::STAGEB + wave * NDMA * 1024;
+    const int last = n - 1 - kb;
 #pragma unroll
-      for (int r = 0; r < KCH; ++r) kr[r] = *(const u32x4*)(Kt + (krow[r] * rs + kcol[r]));
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vr[r] = *(const vchunk*)(Vt + ((4 * vkg + r) * rs + vcg * VC));
-    } else {
-      const int last = n - 1 - kb;
-#pragma unroll
-      for (int r = 0; r < KCH; ++r)
-        kr[r] = *(const u32x4*)(Kt + (min(krow[r], last) * rs + kcol[r]));
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        vr[r] = *(const vchunk*)(Vt + (min(4 * vkg + r, last) * rs + vcg * VC));
+    for (int r = 0; r < NDMA; ++r) {
+      const int row = tail ? min(drow[r], last) : drow[r];
+      __builtin_amdgcn_global_load_lds((const void*)(Kt + (row * rs + kcol[r])),
+                                       (lds_void*)(base + r * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(Vt + (row * rs + vcol[r])),
+                                       (lds_void*)(base + T::TILEB + r * 1024), 16, 0, 0);
     }
   };
-  auto stash = [&](int stage) {
-    unsigned short* Ks = lds + stage * STAGE;
-    unsigned short* Vs = Ks + KT;
-#pragma unroll
-    for (int r = 0; r < KCH; ++r) *(u32x4*)(Ks + krow[r] * KSTR + kcol[r]) = kr[r];
-#pragma unroll
-    for (int c = 0; c < VC; ++c) {
-      u32x2 w;
-      w[0] = half16(vr[0], c) | (half16(vr[1], c) << 16);
-      w[1] = half16(vr[2], c) | (half16(vr[3], c) << 16);
-      *(u32x2*)(Vs + (vcg * VC + c) * VSTR + vpos) = w;
-    }
-  };
+
+  // K fragment (S^T A operand): key row kt*32 + l32, logical chunk 2*ss + g,
+  // stored at chunk (2*ss + g) ^ kswz(row); kswz(kt*32 + l32) == kswz(l32).
+  const int kx = T::kswz(l32);
+  // V fragment (P.V A operand, transposing read): lane j of 16-lane block b
+  // points at row 16t + 8h + 4*(b/2) + j/4 and columns 32*dt + 16*(b%2) +
+  // 4*(j%4) .. +3, so the lane receives d column 32*dt + l32 of keys
+  // 16t + 8h + 4g + 0..3: slots 4h .. 4h+3 of P.V MFMA t.
+  const int vj = lane & 15, vb = lane >> 4;
+  const int vrow = 4 * (vb >> 1) + (vj >> 2);
+  const int vin = 32 * (vb & 1) + 8 * (vj & 3);  // byte offset inside the 64-byte chunk
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -215,8 +197,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
   // ragged last tile (keys >= n get probability 0).
   auto step = [&](auto masked, int stage, int kb) {
     constexpr bool MASKED = decltype(masked)::value;
-    const unsigned short* Ks = lds + stage * STAGE;
-    const unsigned short* Vs = Ks + KT;
+    const lds_u8* Ks = (const lds_u8*)lds + stage * T::STAGEB;
+    const lds_u8* Vs = Ks + T::TILEB;
 
     // S^T tile: two 32-key MFMA tiles; lane holds query l32, keys
     // kt*32 + 8*(i/4) + 4*g + (i%4) in register i.
@@ -225,15 +207,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kt][i] = 0.f;
-    FA_PRIO_HI();
 #pragma unroll
     for (int ss = 0; ss < D / 16; ++ss)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const vec8 a = *(const vec8*)(Ks + (kt * 32 + l32) * KSTR + 16 * ss + 8 * g);
+        const vec8 a = *(const __attribute__((address_space(3))) vec8*)(
+            Ks + (kt * 32 + l32) * T::ROWB + (((2 * ss + g) ^ kx) << 4));
         s[kt] = mfma32x32x16<BF16>(a, qf[ss], s[kt]);
       }
-    FA_PRIO_LO();
 
     if constexpr (MASKED) {
 #pragma unroll
@@ -245,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
         }
     }
 
-    // Row max: four independent max3 chains, then one exchange with lane ^ 32.
+    // Row max: four independent chains, then one exchange with lane ^ 32.
     float mq[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -282,36 +263,38 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
     // O^T += V^T P^T over the 64 keys, 16 keys per MFMA. Slot jj of lane
     // group g in MFMA t is key 16t + 8*(jj/4) + 4g + jj%4, which is S^T
     // register 8*(t%2) + jj of key tile t/2.
-    vec8 pb[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       u32x4 pw;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         pw[q] = pack2<BF16>(s[t >> 1][8 * (t & 1) + 2 * q], s[t >> 1][8 * (t & 1) + 2 * q + 1]);
-      pb[t] = __builtin_bit_cast(vec8, pw);
-    }
-    FA_PRIO_HI();
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
+      const vec8 pb = __builtin_bit_cast(vec8, pw);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const vec8 a = *(const vec8*)(Vs + (dt * 32 + l32) * VSTR + 16 * t + 8 * g);
-        o[dt] = mfma32x32x16<BF16>(a, pb[t], o[dt]);
+        i16x4 hv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int row = 16 * t + 8 * h + vrow;
+          hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lds_i16x4*)(Vs + row * T::ROWB + ((dt ^ T::vswz(row)) << 6) + vin));
+        }
+        const i16x8 a8 = {hv[0][0], hv[0][1], hv[0][2], hv[0][3],
+                          hv[1][0], hv[1][1], hv[1][2], hv[1][3]};
+        o[dt] = mfma32x32x16<BF16>(__builtin_bit_cast(vec8, a8), pb, o[dt]);
       }
-    FA_PRIO_LO();
+    }
   };
 
-  const int nfull = n / BC;                  // tiles with all BC keys valid
+  const int nfull = n / BC;  // tiles with all BC keys valid
   const int tiles = (n + BC - 1) / BC;
-  fetch(0, nfull == 0);
-  stash(0);
+  fetch(0, 0, nfull == 0);
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int j = 0; j < nfull; ++j) {
-    const bool more = (j + 1) < tiles;
-    if (more) fetch((j + 1) * BC, j + 1 == nfull);
+    if (j + 1 < tiles) fetch((j + 1) & 1, (j + 1) * BC, j + 1 == nfull);
     step(std::false_type{}, j & 1, j * BC);
-    if (more) stash((j + 1) & 1);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
   if (nfull < tiles) step(std::true_type{}, nfull & 1, nfull * BC);
