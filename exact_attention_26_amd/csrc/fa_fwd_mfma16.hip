@@ -39,6 +39,21 @@
 
 #include "fa_device.h"
 
+// Build options (defaults are the shipped configuration):
+//   FA_MFMA_ROWSUM_D64 (0): at d = 64 run the row sums on the matrix cores
+//     (a ones-operand MFMA per 16 keys) instead of VALU adds; at d = 128 the
+//     extra accumulator does not fit the register budget of 2 waves/SIMD.
+//   FA_RESCALE_TAU (0): the running max moves (and O, l are rescaled) when
+//     some row's max grew by more than TAU in log2 units of probability; 0 is
+//     the method as written (every increase). TAU > 0 defers small rescales
+//     (same function, fewer multiplies); it is an experiment, off by default.
+#ifndef FA_MFMA_ROWSUM_D64
+#define FA_MFMA_ROWSUM_D64 0
+#endif
+#ifndef FA_RESCALE_TAU
+#define FA_RESCALE_TAU 0
+#endif
+
 namespace fa {
 namespace {
 
@@ -138,38 +153,87 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
     if (qrow < n) w = *(const u32x4*)(Qg + qrow * rs + 16 * s + 8 * g);
     qf[s] = __builtin_bit_cast(vec8, w);
   }
+  // Consume Q here so the compiler waits for these loads before the key
+  // loop; otherwise it places that wait inside the loop, where it would
+  // also stall on the prefetch of the next K/V tile.
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) __asm__ volatile("" : : "v"(qf[s]));
 
-  // Direct-to-LDS copies. Copy r of this wave fills bytes
-  // [1024*(wave*NDMA + r), +1024) of the K (and of the V) tile; lane i
-  // writes 16 bytes at +16*i, i.e. 16-byte slot s of the tile. Slot s is
-  // (row, stored chunk); the lane fetches the logical chunk the swizzle
-  // stores there.
+  // LDS holds two K stages followed by two V stages. K runs one tile ahead
+  // of V: while tile j's P.V reads V stage j%2, the S^T of tile j+1 reads K
+  // stage (j+1)%2, and the copies in flight fill K stage j%2 (tile j+2) and
+  // V stage (j+1)%2 (tile j+1).
+  //
+  // Direct-to-LDS copies: copy r of this wave fills bytes
+  // [1024*(wave*NDMA + r), +1024) of a tile; lane i writes 16 bytes at
+  // +16*i, i.e. 16-byte slot s of the tile. Slot s is (row, stored chunk);
+  // the lane fetches the logical chunk the swizzle stores there.
   constexpr int NDMA = T::DMA_PER_WAVE;
-  int drow[NDMA], kcol[NDMA], vcol[NDMA];
+  // Row and (logical) column of the 16 bytes copy r of this lane moves.
+  auto dma_row = [&](int r) { return ((wave * NDMA + r) * 64 + lane) / T::KCHUNKS; };
+  auto dma_kcol = [&](int r) {
+    const int s = (wave * NDMA + r) * 64 + lane;
+    return ((s % T::KCHUNKS) ^ T::kswz(s / T::KCHUNKS)) * 8;
+  };
+  auto dma_vcol = [&](int r) {
+    const int s = (wave * NDMA + r) * 64 + lane;
+    const int pos = s % T::KCHUNKS;
+    return ((((pos >> 2) ^ T::vswz(s / T::KCHUNKS)) << 2) | (pos & 3)) * 8;
+  };
+#if FA_DMA_PRECOMPUTE
+  unsigned koffb[NDMA], voffb[NDMA];  // byte offsets inside a full tile
 #pragma unroll
   for (int r = 0; r < NDMA; ++r) {
-    const int s = (wave * NDMA + r) * 64 + lane;
-    const int row = s / T::KCHUNKS;
-    const int pos = s % T::KCHUNKS;
-    drow[r] = row;
-    kcol[r] = (pos ^ T::kswz(row)) * 8;
-    vcol[r] = ((((pos >> 2) ^ T::vswz(row)) << 2) | (pos & 3)) * 8;
+    koffb[r] = (unsigned)(dma_row(r) * rs + dma_kcol(r)) * 2u;
+    voffb[r] = (unsigned)(dma_row(r) * rs + dma_vcol(r)) * 2u;
   }
-  // Tile at key kb into LDS stage `stage`. In the ragged last tile (tail)
-  // rows past the end are clamped to row n-1: loads stay in bounds and those
-  // keys are masked out of the scores.
-  auto fetch = [&](int stage, int kb, bool tail) {
-    const unsigned short* Kt = Kg + (int64_t)kb * rs;
-    const unsigned short* Vt = Vg + (int64_t)kb * rs;
-    lds_u8* base = (lds_u8*)lds + stage * T::STAGEB + wave * NDMA * 1024;
-    const int last = n - 1 - kb;
+#define FA_KOFF(r) koffb[r]
+#define FA_VOFF(r) voffb[r]
+#else
+#define FA_KOFF(r) ((unsigned)(dma_row(r) * rs + dma_kcol(r)) * 2u)
+#define FA_VOFF(r) ((unsigned)(dma_row(r) * rs + dma_vcol(r)) * 2u)
+#endif
+  const unsigned lds0 = (unsigned)(uintptr_t)(lds_u8*)lds + (unsigned)(wave * NDMA * 1024);
+  // Copy the K (or V) tile at key kb into LDS at byte `dst`. In the ragged
+  // last tile (tail) rows past the end are clamped to row n-1: loads stay in
+  // bounds and those keys are masked out of the scores.
+  //
+  // The copies are inline asm (global_load_lds_dwordx4, LDS destination in
+  // M0) so the compiler does not treat them as pending writes to every LDS
+  // location and wait for them before unrelated LDS reads; completion is
+  // awaited explicitly (vmcnt(0)) before the barrier that publishes a tile.
+  auto dma = [&](const unsigned short* Gt, unsigned dst, unsigned off) {
+    __asm__ volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(dst), "v"(off), "s"(Gt)
+        : "memory", "m0");
+  };
+  auto fetch_k = [&](int stage, int kb, bool tail) {
+    const unsigned short* Gt = Kg + (int64_t)kb * rs;
+    const unsigned dst = lds0 + stage * T::TILEB;
+    if (!tail) {
 #pragma unroll
-    for (int r = 0; r < NDMA; ++r) {
-      const int row = tail ? min(drow[r], last) : drow[r];
-      __builtin_amdgcn_global_load_lds((const void*)(Kt + (row * rs + kcol[r])),
-                                       (lds_void*)(base + r * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(Vt + (row * rs + vcol[r])),
-                                       (lds_void*)(base + T::TILEB + r * 1024), 16, 0, 0);
+      for (int r = 0; r < NDMA; ++r) dma(Gt, dst + r * 1024, FA_KOFF(r));
+    } else {
+      const int last = n - 1 - kb;
+#pragma unroll
+      for (int r = 0; r < NDMA; ++r)
+        dma(Gt, dst + r * 1024, (unsigned)(min(dma_row(r), last) * rs + dma_kcol(r)) * 2u);
+    }
+  };
+  auto fetch_v = [&](int stage, int kb, bool tail) {
+    const unsigned short* Gt = Vg + (int64_t)kb * rs;
+    const unsigned dst = lds0 + (2 + stage) * T::TILEB;
+    if (!tail) {
+#pragma unroll
+      for (int r = 0; r < NDMA; ++r) dma(Gt, dst + r * 1024, FA_VOFF(r));
+    } else {
+      const int last = n - 1 - kb;
+#pragma unroll
+      for (int r = 0; r < NDMA; ++r)
+        dma(Gt, dst + r * 1024, (unsigned)(min(dma_row(r), last) * rs + dma_vcol(r)) * 2u);
     }
   };
 
@@ -184,25 +248,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
   const int vrow = 4 * (vb >> 1) + (vj >> 2);
   const int vin = 32 * (vb & 1) + 8 * (vj & 3);  // byte offset inside the 64-byte chunk
 
-  f32x16 o[D / 32];
+  f32x16 o[D / 32];  // O^T accumulators: d = 32*t + 8*(i/4) + 4g + i%4, query l32
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
-  float m = -INFINITY;  // running max of raw q.k (scale > 0)
-  float l = 0.f;        // running sum of this lane's half of the keys
+  // Row sums on the matrix cores: one more P.V MFMA per 16 keys with an
+  // all-ones A operand leaves sum_k P[q][k] (over both half-waves' keys) in
+  // every register of lacc; only lacc[0] is carried (and rescaled).
+  constexpr bool kRowSumMfma = FA_MFMA_ROWSUM_D64 && D == 64;
+  f32x16 lacc;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
+  const vec8 ones = __builtin_bit_cast(
+      vec8, (u32x4){pack2<BF16>(1.f, 1.f), pack2<BF16>(1.f, 1.f), pack2<BF16>(1.f, 1.f),
+                    pack2<BF16>(1.f, 1.f)});
+  float l = 0.f;  // VALU row sums: this lane's half of the keys
   const float c2 = p.scale_log2;
 
-  // One key tile: scores, online softmax update, P.V. MASKED marks the
-  // ragged last tile (keys >= n get probability 0).
-  auto step = [&](auto masked, int stage, int kb) {
-    constexpr bool MASKED = decltype(masked)::value;
-    const lds_u8* Ks = (const lds_u8*)lds + stage * T::STAGEB;
-    const lds_u8* Vs = Ks + T::TILEB;
-
-    // S^T tile: two 32-key MFMA tiles; lane holds query l32, keys
-    // kt*32 + 8*(i/4) + 4*g + (i%4) in register i.
-    f32x16 s[2];
+  // S^T of the K tile in stage `stage`: lane holds query l32, keys
+  // kt*32 + 8*(i/4) + 4*g + (i%4) in register i of s[kt].
+  auto qk = [&](int stage, f32x16 (&s)[2]) {
+    const lds_u8* Ks = (const lds_u8*)lds + stage * T::TILEB;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -215,54 +282,52 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
             Ks + (kt * 32 + l32) * T::ROWB + (((2 * ss + g) ^ kx) << 4));
         s[kt] = mfma32x32x16<BF16>(a, qf[ss], s[kt]);
       }
-
-    if constexpr (MASKED) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kb + kt * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key >= n) s[kt][i] = -INFINITY;
-        }
-    }
-
-    // Row max: four independent chains, then one exchange with lane ^ 32.
-    float mq[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const f32x16& a = s[q >> 1];
-      const int b = 8 * (q & 1);
-      mq[q] = fmaxf(fmaxf(fmaxf(a[b + 0], a[b + 1]), fmaxf(a[b + 2], a[b + 3])),
-                    fmaxf(fmaxf(a[b + 4], a[b + 5]), fmaxf(a[b + 6], a[b + 7])));
-    }
-    float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx);
-    const bool grew = mnew > m;
-    const float alpha = grew ? __builtin_amdgcn_exp2f((m - mnew) * c2) : 1.f;
-    const float mc = mnew * c2;
-    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+  };
+  // Keys >= n of the tile at kb score -inf (probability 0).
+  auto mask = [&](f32x16 (&s)[2], int kb) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -mc));
-        s[kt][i] = e;
-        ls[i & 3] += e;
+        const int key = kb + kt * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key >= n) s[kt][i] = -INFINITY;
       }
-    l = l * alpha + ((ls[0] + ls[1]) + (ls[2] + ls[3]));
-    m = mnew;
-    // Rescale the running output only if some lane's max moved (alpha != 1).
-    if (__any(grew)) {
+  };
+  // Max over this lane's 32 scores, then over the partner lane l ^ 32
+  // (v_permlane32_swap exchanges the two half-waves).
+  auto rowmax = [&](const f32x16 (&s)[2]) {
+    float a = fmaxf(s[0][0], s[0][1]), b = fmaxf(s[1][0], s[1][1]);
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+    for (int i = 2; i < 16; i += 2) {
+      a = fmaxf(fmaxf(a, s[0][i]), s[0][i + 1]);
+      b = fmaxf(fmaxf(b, s[1][i]), s[1][i + 1]);
     }
-
-    // O^T += V^T P^T over the 64 keys, 16 keys per MFMA. Slot jj of lane
-    // group g in MFMA t is key 16t + 8*(jj/4) + 4g + jj%4, which is S^T
-    // register 8*(t%2) + jj of key tile t/2.
+    const float x = fmaxf(a, b);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                     false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+  };
+  // p = exp2(s*c - m*c) in place; returns this lane's sum of p (VALU sums).
+  auto expo = [&](f32x16 (&s)[2], float mc) {
+    float ls[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[kt][i] = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -mc));
+        if (kt == 0 && i < 4)
+          ls[i] = s[kt][i];
+        else
+          ls[i & 3] += s[kt][i];
+      }
+    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+  // O^T += V^T P^T over the 64 keys of the V tile in stage `stage`, 16 keys
+  // per MFMA, and the row sums. Slot jj of lane group g in MFMA t is key
+  // 16t + 8*(jj/4) + 4g + jj%4, which is S^T register 8*(t%2) + jj of key
+  // tile t/2.
+  auto pv = [&](int stage, const f32x16 (&s)[2]) {
+    const lds_u8* Vs = (const lds_u8*)lds + (2 + stage) * T::TILEB;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       u32x4 pw;
@@ -283,24 +348,99 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
                           hv[1][0], hv[1][1], hv[1][2], hv[1][3]};
         o[dt] = mfma32x32x16<BF16>(__builtin_bit_cast(vec8, a8), pb, o[dt]);
       }
+      if constexpr (kRowSumMfma) lacc = mfma32x32x16<BF16>(ones, pb, lacc);
     }
   };
 
   const int nfull = n / BC;  // tiles with all BC keys valid
   const int tiles = (n + BC - 1) / BC;
-  fetch(0, 0, nfull == 0);
+
+  // Prologue: K and V of tile 0 and K of tile 1 in flight, then S^T of
+  // tile 0 and its row max.
+  fetch_k(0, 0, nfull == 0);
+  fetch_v(0, 0, nfull == 0);
+  if (tiles > 1) fetch_k(1, BC, nfull == 1);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int j = 0; j < nfull; ++j) {
-    if (j + 1 < tiles) fetch((j + 1) & 1, (j + 1) * BC, j + 1 == nfull);
-    step(std::false_type{}, j & 1, j * BC);
-    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  f32x16 sA[2], sB[2];  // scores of the current / next tile, swapping roles
+  qk(0, sA);
+  float m = rowmax(sA);  // running max of raw q.k (scale > 0)
+
+  // Iteration j (stage parity P = j % 2): the softmax VALU work of tile j
+  // is interleaved with the S^T MFMAs of tile j+1, and the row max of tile
+  // j+1 with the P.V MFMAs of tile j. HAS_NEXT: a tile j+1 exists.
+  //
+  // The ragged last tile needs no special handling until its exponentials:
+  // its rows past the end are copies of key row n-1, so their scores equal a
+  // real score and leave the running max unchanged; they are masked to
+  // probability 0 just before the exp2 in the final iteration.
+  auto iteration = [&](auto has_next, auto parity, int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    constexpr bool HN = decltype(has_next)::value;
+    constexpr int P = decltype(parity)::value;
+    // Keep each iteration its own scheduling region (bounds register
+    // pressure: the scheduler would otherwise hoist the next iteration's
+    // loads and spill).
+    if constexpr (HN) {
+      if (j + 2 < tiles) fetch_k(P, (j + 2) * BC, j + 2 == nfull);
+      fetch_v(1 - P, (j + 1) * BC, j + 1 == nfull);
+      qk(1 - P, sn);
+    }
+    if constexpr (!HN) {
+      if (nfull < tiles) mask(sc, j * BC);
+    }
+    const float lsum = expo(sc, m * c2);
+    pv(P, sc);
+    if constexpr (!kRowSumMfma) l += lsum;
+    if constexpr (HN) {
+      // The running max moves when some row of the wave saw a larger score
+      // (by more than FA_RESCALE_TAU in log2 units; 0 = any increase): then
+      // O and l of every row are brought to its new max by
+      // alpha = exp2((m_old - m_new) * c), which is 1 for rows whose max
+      // did not move. The branch is uniform across the wave.
+      const float mx = rowmax(sn);
+      if (__any((mx - m) * c2 > (float)FA_RESCALE_TAU)) {
+        const float mnew = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c2);
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+        if constexpr (kRowSumMfma)
+          lacc[0] *= alpha;
+        else
+          l *= alpha;
+        m = mnew;
+      }
+      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+  };
+  using T0 = std::integral_constant<int, 0>;
+  using T1 = std::integral_constant<int, 1>;
+  const std::true_type Y;
+  const std::false_type N;
+
+  int j = 0;
+  for (; j + 2 < tiles; j += 2) {  // pairs of iterations that both have a next tile
+    iteration(Y, T0{}, j, sA, sB);
+    iteration(Y, T1{}, j + 1, sB, sA);
   }
-  if (nfull < tiles) step(std::true_type{}, nfull & 1, nfull * BC);
+  // j is even here and the current scores are in sA.
+  if (j + 1 < tiles) {
+    iteration(Y, T0{}, j, sA, sB);
+    iteration(N, T1{}, j + 1, sB, sA);
+  } else {
+    iteration(N, T0{}, j, sA, sB);
+  }
+  if constexpr (kRowSumMfma) {
+    l = lacc[0];  // already the sum over both half-waves' keys
+  } else {        // add the partner half-wave's partial sum
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l),
+                                                     false, false);
+    l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
 
   // Write-back: divide once by l, L = m*scale + ln l.
-  l += __shfl_xor(l, 32);
   if (qrow < n) {
     const float inv = 1.f / l;
     unsigned short* orow = Og + qrow * rs;
