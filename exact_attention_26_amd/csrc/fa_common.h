@@ -39,8 +39,13 @@ hipError_t launch_fwd_f32(const FwdParams& p, int d, bool varlen, hipStream_t st
 hipError_t launch_fwd_mfma16(const FwdParams& p, int d, bool bf16, bool varlen,
                              hipStream_t stream);
 
-// Rows of Q owned by one workgroup of each kernel (sizes the grid).
+// Rows of Q owned by one workgroup of each kernel (sizes the grid). The
+// 16-bit kernel runs kWaves16 waves of 32 query rows each.
+#ifndef FA_WAVES16
+#define FA_WAVES16 8
+#endif
+constexpr int kWaves16 = FA_WAVES16;
 constexpr int kRowsPerBlockF32 = 128;
-constexpr int kRowsPerBlock16 = 128;
+constexpr int kRowsPerBlock16 = 32 * kWaves16;
 
 }  // namespace fa

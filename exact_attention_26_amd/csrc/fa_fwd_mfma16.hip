@@ -9,8 +9,9 @@
 // Scores never leave the chip.
 //
 // How it maps onto CDNA4:
-//  * 256 threads = 4 waves; each wave owns 32 query rows, so a workgroup
-//    owns Br = 128 rows. Keys are streamed in tiles of Bc = 64.
+//  * 512 threads = 8 waves (2 per SIMD); each wave owns 32 query rows, so a
+//    workgroup owns Br = 256 rows and re-reads K/V once per 256 queries.
+//    Keys are streamed in tiles of Bc = 64.
 //  * Scores are computed transposed, S^T = K Q^T, with
 //    v_mfma_f32_32x32x16_{bf16,f16}: the accumulator puts one query per
 //    lane (column n = lane % 32) and 16 keys per lane, so the row max and
@@ -57,8 +58,8 @@
 namespace fa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
+constexpr int kWaves = kWaves16;
+constexpr int kThreads = 64 * kWaves;
 constexpr int BR = kRowsPerBlock16;  // query rows per workgroup (32 per wave)
 constexpr int BC = 64;               // keys per tile
 
