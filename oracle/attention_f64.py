@@ -65,10 +65,10 @@ def _f64(x) -> np.ndarray:
 # [FS] STAGE 1: softmax with the max subtracted for overflow safety.
 # ---------------------------------------------------------------------------
 def softmax(x, axis: int = -1) -> np.ndarray:
-    x = _f64(x)
-    top = np.max(x, axis=axis, keepdims=True)
-    e = np.exp(x - top)
-    return e / np.sum(e, axis=axis, keepdims=True)
+    z = _f64(x)
+    z = z - z.max(axis=axis, keepdims=True)   # largest entry becomes 0
+    w = np.exp(z)
+    return w / w.sum(axis=axis, keepdims=True)
 
 
 def scores_to_weights(S):
@@ -89,17 +89,15 @@ def scores_to_weights(S):
 # max, the old sum is brought to the new baseline by exp(m_old - m_new).
 # ---------------------------------------------------------------------------
 def online_softmax(row, block: int = 8, rescale: bool = True) -> np.ndarray:
-    row = _f64(row).reshape(-1)
-    m = -np.inf
-    l = 0.0
-    for start in range(0, row.size, block):
-        chunk = row[start:start + block]
-        m_next = max(m, float(chunk.max()))
-        if rescale and m > -np.inf:
-            l *= np.exp(m - m_next)
-        l += float(np.exp(chunk - m_next).sum())
-        m = m_next
-    return np.exp(row - m) / l
+    x = _f64(row).reshape(-1)
+    ref, total = -np.inf, 0.0          # running max, sum of exp(x - ref)
+    for b in range(0, x.size, block):
+        part = x[b:b + block]
+        top = max(ref, float(part.max()))
+        carry = float(np.exp(ref - top)) if (rescale and np.isfinite(ref)) else 1.0
+        total = total * carry + float(np.exp(part - top).sum())
+        ref = top
+    return np.exp(x - ref) / total
 
 
 # ---------------------------------------------------------------------------
@@ -181,45 +179,48 @@ def attention_varlen_rows(q, k, v, cu_seqlens, scale: float, seq: int, h: int, r
 # ---------------------------------------------------------------------------
 # O2: the tiled online algorithm, [FS] STAGE 4 with [KV]'s scale and L.
 #
-# Outer loop over Br-row blocks of Q, inner loop over Bc-column blocks of
-# K and V. Per query row it carries m (running max of the scaled scores),
-# l (running sum of exp(s - m)) and the unnormalised output row. When a
-# block raises m, both l and the output are multiplied by exp(m_old - m_new)
-# (a row that has seen nothing yet, m_old = -inf, gets factor 0). At the end
-# O = O / l once and L = m + ln l.
+# The query rows are cut into blocks of Br and the keys into blocks of Bc;
+# query blocks are the outer loop. For every query row of a block three
+# running quantities are kept while the key blocks go by: the largest scaled
+# score seen so far (run_max), the sum of exp(score - run_max) (run_sum) and
+# the matching unnormalised weighted sum of value rows (acc). A key block
+# with a larger score moves run_max; the old run_sum and acc were formed
+# against the old maximum, so both are first multiplied by
+# exp(old_max - new_max) (0 for a row that has not seen any key). After the
+# last key block the row is divided by run_sum once, and its logsumexp is
+# run_max + ln(run_sum).
 #
 # `rescale=False` is [FS]'s planted bug (sums taken against different
-# baselines); `rescale_o=False` rescales l but not O. Both must fail the
-# equivalence pins.
+# baselines); `rescale_o=False` corrects run_sum but not acc. Both must fail
+# the equivalence pins.
 # ---------------------------------------------------------------------------
 def attention_tiled(Q, K, V, scale: float, Br: int = 64, Bc: int = 64,
                     rescale: bool = True, rescale_o: bool = True):
     Q, K, V = _f64(Q), _f64(K), _f64(V)
-    n = Q.shape[0]
-    m_keys = K.shape[0]
-    O = np.zeros((n, V.shape[1]), dtype=np.float64)
-    L = np.zeros((n,), dtype=np.float64)
-    for i in range(0, n, Br):
-        Qi = Q[i:i + Br]
-        rows = Qi.shape[0]
-        Oi = np.zeros((rows, V.shape[1]))
-        mi = np.full((rows, 1), -np.inf)
-        li = np.zeros((rows, 1))
-        for j in range(0, m_keys, Bc):
-            Kj, Vj = K[j:j + Bc], V[j:j + Bc]
-            Sij = scale * (Qi @ Kj.T)
-            m_new = np.maximum(mi, Sij.max(axis=1, keepdims=True))
-            Pij = np.exp(Sij - m_new)
+    n_q, n_k = Q.shape[0], K.shape[0]
+    out = np.empty((n_q, V.shape[1]), dtype=np.float64)
+    lse = np.empty((n_q,), dtype=np.float64)
+    key_blocks = [(a, min(a + Bc, n_k)) for a in range(0, n_k, Bc)]
+    for r0 in range(0, n_q, Br):
+        r1 = min(r0 + Br, n_q)
+        q_blk = Q[r0:r1]
+        run_max = np.full(r1 - r0, -np.inf)
+        run_sum = np.zeros(r1 - r0)
+        acc = np.zeros((r1 - r0, V.shape[1]))
+        for (c0, c1) in key_blocks:
+            scores = scale * (q_blk @ K[c0:c1].T)          # (rows, keys) block
+            new_max = np.maximum(run_max, scores.max(axis=1))
+            w = np.exp(scores - new_max[:, None])           # unnormalised weights
             if rescale:
-                with np.errstate(invalid="ignore"):
-                    alpha = np.exp(mi - m_new)
-                alpha[np.isneginf(mi)] = 0.0
-                li = alpha * li + Pij.sum(axis=1, keepdims=True)
-                Oi = (alpha * Oi if rescale_o else Oi) + Pij @ Vj
+                fix = np.zeros_like(run_max)
+                seen = np.isfinite(run_max)
+                fix[seen] = np.exp(run_max[seen] - new_max[seen])
+                run_sum = fix * run_sum + w.sum(axis=1)
+                acc = (fix[:, None] * acc if rescale_o else acc) + w @ V[c0:c1]
             else:
-                li = li + Pij.sum(axis=1, keepdims=True)
-                Oi = Oi + Pij @ Vj
-            mi = m_new
-        O[i:i + rows] = Oi / li
-        L[i:i + rows] = mi[:, 0] + np.log(li[:, 0])
-    return O, L
+                run_sum = run_sum + w.sum(axis=1)
+                acc = acc + w @ V[c0:c1]
+            run_max = new_max
+        out[r0:r1] = acc / run_sum[:, None]
+        lse[r0:r1] = run_max + np.log(run_sum)
+    return out, lse
