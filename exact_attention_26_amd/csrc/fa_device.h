@@ -36,7 +36,11 @@ struct WorkUnit {
   int64_t lse_base;  // element offset of row 0 of this head in L
 };
 
-// Logical id order: head-major (all Q-blocks of a head are consecutive).
+// Logical id order: the Q-blocks of one (batch or sequence, head) are
+// consecutive, so xcd_remap keeps them on one XCD (one L2 holds that head's
+// K/V). Dense units run batch-major; varlen units run head-major, so that
+// every XCD's contiguous share of units holds all sequences (for a few
+// heads) and the XCDs get equal work whatever the length mix.
 // Returns false when the unit lies past the end of its sequence (varlen).
 template <bool VARLEN>
 __device__ __forceinline__ bool resolve_unit(const FwdParams& p, int rows_per_block,
@@ -44,8 +48,8 @@ __device__ __forceinline__ bool resolve_unit(const FwdParams& p, int rows_per_bl
   const int id = xcd_remap((int)blockIdx.x, (int)gridDim.x);
   const int qb = id % p.q_blocks;
   const int rest = id / p.q_blocks;
-  const int h = rest % p.H;
-  const int b = rest / p.H;
+  const int h = VARLEN ? rest / p.B : rest % p.H;
+  const int b = VARLEN ? rest % p.B : rest / p.H;
   u.q0 = qb * rows_per_block;
   if (VARLEN) {
     const int start = p.cu_seqlens[b];

@@ -54,6 +54,18 @@
 #ifndef FA_RESCALE_TAU
 #define FA_RESCALE_TAU 0
 #endif
+#ifndef FA_SCHED
+#define FA_SCHED 0
+#endif
+#ifndef FA_SCHED_AH
+#define FA_SCHED_AH 4
+#endif
+#ifndef FA_SCHED_VA
+#define FA_SCHED_VA 6
+#endif
+#ifndef FA_SCHED_VB
+#define FA_SCHED_VB 3
+#endif
 
 namespace fa {
 namespace {
@@ -399,6 +411,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
       // alpha = exp2((m_old - m_new) * c), which is 1 for rows whose max
       // did not move. The branch is uniform across the wave.
       const float mx = rowmax(sn);
+#if FA_SCHED
+      // Interleave: S^T MFMAs of tile j+1 with the softmax VALU of tile j,
+      // then P.V MFMAs of tile j with the row max of tile j+1; LDS reads run
+      // a few MFMAs ahead of their use.
+      __builtin_amdgcn_sched_group_barrier(0x100, FA_SCHED_AH, 0);
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, FA_SCHED_VA, 0);
+        if (i + FA_SCHED_AH < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * FA_SCHED_AH, 0);
+#pragma unroll
+      for (int i = 0; i < D / 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, FA_SCHED_VB, 0);
+        if (i + FA_SCHED_AH < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+#endif
       if (__any((mx - m) * c2 > (float)FA_RESCALE_TAU)) {
         const float mnew = fmaxf(m, mx);
         const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c2);
