@@ -18,11 +18,18 @@
 //    row sum are in-lane reductions plus one exchange with lane ^ 32.
 //  * Q stays in VGPRs for the whole loop as the B operand of S^T.
 //  * P = exp2(S*c - m*c) (c = scale*log2 e) is rounded to the storage dtype
-//    and fed from the S^T accumulator registers straight into the P.V
-//    MFMA as its B operand (O^T = V^T P^T): no LDS round trip for P.
+//    and fed from registers straight into the P.V MFMA as its B operand
+//    (O^T = V^T P^T): no LDS round trip for P.
+//  * Ping-pong between the two waves of a SIMD: waves w and w+4 (measured:
+//    they share a SIMD) run half a step apart, and each step of a wave is a
+//    matrix half (MFMAs and LDS reads only) and a softmax half (VALU only),
+//    separated by workgroup barriers. Exponentials issued by the wave that
+//    also issues the MFMAs barely overlap them, while the VALU of one wave
+//    and the MFMAs of the other do.
 //  * K and V tiles travel HBM -> LDS with global_load_lds_dwordx4 (no
-//    staging registers, no LDS write instructions). Both stay row-major in
-//    LDS with an XOR swizzle of their columns:
+//    staging registers, no LDS write instructions), issued by waves 4-7 at
+//    the start of their softmax half. Both stay row-major in LDS with an
+//    XOR swizzle of their columns:
 //      K: 16-byte chunk c of row r sits at chunk c ^ kswz(r); a lane reads
 //         one 16-byte chunk of one key row per S^T MFMA (ds_read_b128);
 //      V: 64-byte chunk c of row r sits at chunk c ^ vswz(r); the P.V
@@ -31,40 +38,31 @@
 //         lane l receives element l%4 of the 4-element vectors loaded by
 //         lanes l/4, l/4+4, l/4+8 and l/4+12.
 //    Both read patterns are free of LDS bank conflicts.
-//  * Two LDS stages: tile j+1 streams into one stage while tile j is
-//    computed from the other; one barrier per tile.
+//  * Two LDS stages each for K and V, K one tile ahead of V.
 //  * O (fp32) lives in MFMA accumulators for the whole loop, one query per
 //    lane, so the rescale by alpha is a per-lane scalar multiply, skipped
-//    when no lane's running max moved.
+//    when no row's running max moved by more than FA_RESCALE_TAU.
 #include <type_traits>
 
 #include "fa_device.h"
 
 // Build options (defaults are the shipped configuration):
-//   FA_MFMA_ROWSUM_D64 (0): at d = 64 run the row sums on the matrix cores
-//     (a ones-operand MFMA per 16 keys) instead of VALU adds; at d = 128 the
-//     extra accumulator does not fit the register budget of 2 waves/SIMD.
-//   FA_RESCALE_TAU (0): the running max moves (and O, l are rescaled) when
-//     some row's max grew by more than TAU in log2 units of probability; 0 is
-//     the method as written (every increase). TAU > 0 defers small rescales
-//     (same function, fewer multiplies); it is an experiment, off by default.
-#ifndef FA_MFMA_ROWSUM_D64
-#define FA_MFMA_ROWSUM_D64 0
-#endif
+//   FA_RESCALE_TAU (8): the reference max m of the running sums moves (and
+//     O, l are rescaled by exp2((m_old - m_new) * c)) only when some row's
+//     max exceeds it by more than TAU in log2 units. O/l and L = m + ln l
+//     are the same for any reference, so this changes rounding only; p stays
+//     below 2^TAU (no overflow in fp32, bf16 or fp16). 0 rescales on every
+//     increase of the max.
+//   FA_PP_PRIO (1): s_setprio of a wave during its matrix half.
+//   FA_PP_AHEAD (2): MFMA steps between an LDS operand read and its use.
 #ifndef FA_RESCALE_TAU
-#define FA_RESCALE_TAU 0
+#define FA_RESCALE_TAU 8
 #endif
-#ifndef FA_SCHED
-#define FA_SCHED 0
+#ifndef FA_PP_PRIO
+#define FA_PP_PRIO 1
 #endif
-#ifndef FA_SCHED_AH
-#define FA_SCHED_AH 4
-#endif
-#ifndef FA_SCHED_VA
-#define FA_SCHED_VA 6
-#endif
-#ifndef FA_SCHED_VB
-#define FA_SCHED_VB 3
+#ifndef FA_PP_AHEAD
+#define FA_PP_AHEAD 2
 #endif
 
 namespace fa {
@@ -74,6 +72,8 @@ constexpr int kWaves = kWaves16;
 constexpr int kThreads = 64 * kWaves;
 constexpr int BR = kRowsPerBlock16;  // query rows per workgroup (32 per wave)
 constexpr int BC = 64;               // keys per tile
+// Waves that issue the K/V copies (group B, waves 4-7).
+constexpr int kDmaWaves = 4;
 
 template <bool BF16>
 struct Elem;
@@ -129,7 +129,7 @@ struct Tile {
   static constexpr int ROWS_PER_256 = 256 / ROWB;    // rows sharing one 256-byte bank sweep
   static constexpr int KCHUNKS = ROWB / 16;          // 16-byte chunks per row
   static constexpr int VCHUNKS = ROWB / 64;          // 64-byte chunks per row
-  static constexpr int DMA_PER_WAVE = TILEB / 1024 / kWaves;  // 1 KiB copies per wave
+  static constexpr int DMA_PER_WAVE = TILEB / 1024 / kDmaWaves;  // 1 KiB copies per wave
   // Rows read together get distinct chunk positions, hence distinct banks.
   __device__ static int kswz(int r) { return (r / ROWS_PER_256) & (KCHUNKS - 1); }
   __device__ static int vswz(int r) { return (r / ROWS_PER_256) & (VCHUNKS - 1); }
@@ -182,31 +182,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
   // +16*i, i.e. 16-byte slot s of the tile. Slot s is (row, stored chunk);
   // the lane fetches the logical chunk the swizzle stores there.
   constexpr int NDMA = T::DMA_PER_WAVE;
+  const int dwave = wave % kDmaWaves;  // index among the copying waves
   // Row and (logical) column of the 16 bytes copy r of this lane moves.
-  auto dma_row = [&](int r) { return ((wave * NDMA + r) * 64 + lane) / T::KCHUNKS; };
+  auto dma_row = [&](int r) { return ((dwave * NDMA + r) * 64 + lane) / T::KCHUNKS; };
   auto dma_kcol = [&](int r) {
-    const int s = (wave * NDMA + r) * 64 + lane;
+    const int s = (dwave * NDMA + r) * 64 + lane;
     return ((s % T::KCHUNKS) ^ T::kswz(s / T::KCHUNKS)) * 8;
   };
   auto dma_vcol = [&](int r) {
-    const int s = (wave * NDMA + r) * 64 + lane;
+    const int s = (dwave * NDMA + r) * 64 + lane;
     const int pos = s % T::KCHUNKS;
     return ((((pos >> 2) ^ T::vswz(s / T::KCHUNKS)) << 2) | (pos & 3)) * 8;
   };
-#if FA_DMA_PRECOMPUTE
-  unsigned koffb[NDMA], voffb[NDMA];  // byte offsets inside a full tile
-#pragma unroll
-  for (int r = 0; r < NDMA; ++r) {
-    koffb[r] = (unsigned)(dma_row(r) * rs + dma_kcol(r)) * 2u;
-    voffb[r] = (unsigned)(dma_row(r) * rs + dma_vcol(r)) * 2u;
-  }
-#define FA_KOFF(r) koffb[r]
-#define FA_VOFF(r) voffb[r]
-#else
 #define FA_KOFF(r) ((unsigned)(dma_row(r) * rs + dma_kcol(r)) * 2u)
 #define FA_VOFF(r) ((unsigned)(dma_row(r) * rs + dma_vcol(r)) * 2u)
-#endif
-  const unsigned lds0 = (unsigned)(uintptr_t)(lds_u8*)lds + (unsigned)(wave * NDMA * 1024);
+  const unsigned lds0 = (unsigned)(uintptr_t)(lds_u8*)lds + (unsigned)(dwave * NDMA * 1024);
   // Copy the K (or V) tile at key kb into LDS at byte `dst`. In the ragged
   // last tile (tail) rows past the end are clamped to row n-1: loads stay in
   // bounds and those keys are masked out of the scores.
@@ -266,16 +256,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
   for (int t = 0; t < D / 32; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
-  // Row sums on the matrix cores: one more P.V MFMA per 16 keys with an
-  // all-ones A operand leaves sum_k P[q][k] (over both half-waves' keys) in
-  // every register of lacc; only lacc[0] is carried (and rescaled).
-  constexpr bool kRowSumMfma = FA_MFMA_ROWSUM_D64 && D == 64;
-  f32x16 lacc;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
-  const vec8 ones = __builtin_bit_cast(
-      vec8, (u32x4){pack2<BF16>(1.f, 1.f), pack2<BF16>(1.f, 1.f), pack2<BF16>(1.f, 1.f),
-                    pack2<BF16>(1.f, 1.f)});
   float l = 0.f;  // VALU row sums: this lane's half of the keys
   const float c2 = p.scale_log2;
 
@@ -335,138 +315,158 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
       }
     return (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
-  // O^T += V^T P^T over the 64 keys of the V tile in stage `stage`, 16 keys
-  // per MFMA, and the row sums. Slot jj of lane group g in MFMA t is key
-  // 16t + 8*(jj/4) + 4g + jj%4, which is S^T register 8*(t%2) + jj of key
-  // tile t/2.
-  auto pv = [&](int stage, const f32x16 (&s)[2]) {
-    const lds_u8* Vs = (const lds_u8*)lds + (2 + stage) * T::TILEB;
+
+  const int nfull = n / BC;  // tiles with all BC keys valid
+  const int tiles = (n + BC - 1) / BC;
+
+  static_assert(kWaves == 8, "ping-pong pairs waves w and w+4 on one SIMD");
+  // Ping-pong: waves 0-3 (group A) and 4-7 (group B) share the four SIMDs,
+  // one of each per SIMD, and run half a step apart. Between two workgroup
+  // barriers one wave of every SIMD is in its matrix half (MFMAs only: S^T
+  // of tile t+1 and P.V of tile t) while the other is in its softmax half
+  // (VALU only: row max, rescale, exponentials, row sums, P in the storage
+  // dtype); at the next barrier they swap. The matrix core and the VALU of
+  // a SIMD thus work for different waves at the same time, which overlaps
+  // far better than MFMAs and exponentials issued by one wave.
+  const bool grp_a = wave < 4;
+  vec8 pb[4];           // P of the current tile, storage dtype: P.V B operands
+  float m = -INFINITY;  // running max of raw q.k (scale > 0)
+  f32x16 sc[2];         // scores of the next tile
+
+  // Softmax half for the score tile in sc (keys kb..kb+63): row max, rescale
+  // of O and l when some row's max moved, exponentials, row sums, P packed.
+  auto softmax = [&](bool ragged, int kb) __attribute__((always_inline)) {
+    if (ragged) mask(sc, kb);
+    const float mx = rowmax(sc);
+    if (__any((mx - m) * c2 > (float)FA_RESCALE_TAU)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c2);  // 0 on the first tile
+#pragma unroll
+      for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+      l *= alpha;
+      m = mnew;
+    }
+    // fp32 adds for the row sum (a packed bf16 dot2 would wait for the
+    // matrix pipe, which the partner wave keeps busy).
+    l += expo(sc, m * c2);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       u32x4 pw;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        pw[q] = pack2<BF16>(s[t >> 1][8 * (t & 1) + 2 * q], s[t >> 1][8 * (t & 1) + 2 * q + 1]);
-      const vec8 pb = __builtin_bit_cast(vec8, pw);
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
-        i16x4 hv[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int row = 16 * t + 8 * h + vrow;
-          hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (lds_i16x4*)(Vs + row * T::ROWB + ((dt ^ T::vswz(row)) << 6) + vin));
-        }
-        const i16x8 a8 = {hv[0][0], hv[0][1], hv[0][2], hv[0][3],
-                          hv[1][0], hv[1][1], hv[1][2], hv[1][3]};
-        o[dt] = mfma32x32x16<BF16>(__builtin_bit_cast(vec8, a8), pb, o[dt]);
-      }
-      if constexpr (kRowSumMfma) lacc = mfma32x32x16<BF16>(ones, pb, lacc);
+        pw[q] = pack2<BF16>(sc[t >> 1][8 * (t & 1) + 2 * q], sc[t >> 1][8 * (t & 1) + 2 * q + 1]);
+      pb[t] = __builtin_bit_cast(vec8, pw);
+      // Finish P here: without this the compiler sinks the exponentials past
+      // the barrier into the next matrix half, next to their use.
+      __asm__ volatile("" : "+v"(pb[t]));
     }
+    __asm__ volatile("" : "+v"(l));
   };
-
-  const int nfull = n / BC;  // tiles with all BC keys valid
-  const int tiles = (n + BC - 1) / BC;
-
-  // Prologue: K and V of tile 0 and K of tile 1 in flight, then S^T of
-  // tile 0 and its row max.
-  fetch_k(0, 0, nfull == 0);
-  fetch_v(0, 0, nfull == 0);
-  if (tiles > 1) fetch_k(1, BC, nfull == 1);
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  f32x16 sA[2], sB[2];  // scores of the current / next tile, swapping roles
-  qk(0, sA);
-  float m = rowmax(sA);  // running max of raw q.k (scale > 0)
-
-  // Iteration j (stage parity P = j % 2): the softmax VALU work of tile j
-  // is interleaved with the S^T MFMAs of tile j+1, and the row max of tile
-  // j+1 with the P.V MFMAs of tile j. HAS_NEXT: a tile j+1 exists.
-  //
-  // The ragged last tile needs no special handling until its exponentials:
-  // its rows past the end are copies of key row n-1, so their scores equal a
-  // real score and leave the running max unchanged; they are masked to
-  // probability 0 just before the exp2 in the final iteration.
-  auto iteration = [&](auto has_next, auto parity, int j, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+  // Matrix half of step t (stage parity P = t % 2): S^T of tile t+1 into sc
+  // from K stage 1-P (when HN) and O^T += V^T P^T of tile t from V stage P,
+  // the two MFMA streams interleaved.
+  auto matrix = [&](auto has_next, auto parity) {
     constexpr bool HN = decltype(has_next)::value;
     constexpr int P = decltype(parity)::value;
-    // Keep each iteration its own scheduling region (bounds register
-    // pressure: the scheduler would otherwise hoist the next iteration's
-    // loads and spill).
-    if constexpr (HN) {
-      if (j + 2 < tiles) fetch_k(P, (j + 2) * BC, j + 2 == nfull);
-      fetch_v(1 - P, (j + 1) * BC, j + 1 == nfull);
-      qk(1 - P, sn);
-    }
-    if constexpr (!HN) {
-      if (nfull < tiles) mask(sc, j * BC);
-    }
-    const float lsum = expo(sc, m * c2);
-    pv(P, sc);
-    if constexpr (!kRowSumMfma) l += lsum;
-    if constexpr (HN) {
-      // The running max moves when some row of the wave saw a larger score
-      // (by more than FA_RESCALE_TAU in log2 units; 0 = any increase): then
-      // O and l of every row are brought to its new max by
-      // alpha = exp2((m_old - m_new) * c), which is 1 for rows whose max
-      // did not move. The branch is uniform across the wave.
-      const float mx = rowmax(sn);
-#if FA_SCHED
-      // Interleave: S^T MFMAs of tile j+1 with the softmax VALU of tile j,
-      // then P.V MFMAs of tile j with the row max of tile j+1; LDS reads run
-      // a few MFMAs ahead of their use.
-      __builtin_amdgcn_sched_group_barrier(0x100, FA_SCHED_AH, 0);
-#pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, FA_SCHED_VA, 0);
-        if (i + FA_SCHED_AH < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    const lds_u8* Ks = (const lds_u8*)lds + (1 - P) * T::TILEB;
+    const lds_u8* Vs = (const lds_u8*)lds + (2 + P) * T::TILEB;
+    // Operand reads run FA_PP_AHEAD steps ahead of their MFMAs in rotating
+    // registers; sched_barrier keeps the compiler from hoisting them all.
+    constexpr int NSTEP = D / 8, DT = D / 32, AH = FA_PP_AHEAD, NB = AH + 1;
+    vec8 ka[NB];
+    i16x4 va[NB][2];
+    auto read = [&](int i) {
+      if constexpr (HN) {
+        const int ss = i >> 1, kt = i & 1;
+        ka[i % NB] = *(const __attribute__((address_space(3))) vec8*)(
+            Ks + (kt * 32 + l32) * T::ROWB + (((2 * ss + g) ^ kx) << 4));
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * FA_SCHED_AH, 0);
+      const int t = i / DT, dt = i % DT;
 #pragma unroll
-      for (int i = 0; i < D / 8; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, FA_SCHED_VB, 0);
-        if (i + FA_SCHED_AH < D / 8) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      for (int h = 0; h < 2; ++h) {
+        const int row = 16 * t + 8 * h + vrow;
+        va[i % NB][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(Vs + row * T::ROWB + ((dt ^ T::vswz(row)) << 6) + vin));
       }
-#endif
-      if (__any((mx - m) * c2 > (float)FA_RESCALE_TAU)) {
-        const float mnew = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c2);
+    };
+    __builtin_amdgcn_s_setprio(FA_PP_PRIO);
 #pragma unroll
-        for (int t = 0; t < D / 32; ++t)
+    for (int i = 0; i < AH; ++i) read(i);
 #pragma unroll
-          for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-        if constexpr (kRowSumMfma)
-          lacc[0] *= alpha;
-        else
-          l *= alpha;
-        m = mnew;
+    for (int i = 0; i < NSTEP; ++i) {
+      if (i + AH < NSTEP) read(i + AH);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (HN) {
+        const int ss = i >> 1, kt = i & 1;
+        sc[kt] = mfma32x32x16<BF16>(ka[i % NB], qf[ss], ss == 0 ? f32x16{} : sc[kt]);
       }
-      __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      const int t = i / DT, dt = i % DT;
+      const i16x8 a8 = {va[i % NB][0][0], va[i % NB][0][1], va[i % NB][0][2], va[i % NB][0][3],
+                        va[i % NB][1][0], va[i % NB][1][1], va[i % NB][1][2], va[i % NB][1][3]};
+      o[dt] = mfma32x32x16<BF16>(__builtin_bit_cast(vec8, a8), pb[t], o[dt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
   };
+  // Copies for step t (stage parity P): K of tile t+2 into K stage P (it
+  // held K of tile t, last read in step t-1) and V of tile t+1 into V stage
+  // 1-P (it held V of tile t-1, last read in step t-1).
+  auto prefetch = [&](auto parity, int t) {
+    constexpr int P = decltype(parity)::value;
+    if (t + 2 < tiles) fetch_k(P, (t + 2) * BC, t + 2 == nfull);
+    if (t + 1 < tiles) fetch_v(1 - P, (t + 1) * BC, t + 1 == nfull);
+  };
+  // Step t: [matrix(t)] | [softmax of tile t+1] |. Group B runs every step
+  // one half-step (one barrier) after group A, so on each SIMD the matrix
+  // half of one wave meets the softmax half of the other. Group B issues
+  // the copies for step t+1 at the start of its softmax half of step t and
+  // waits for them at the end of its matrix half of step t+1; that is
+  // before the barrier after which group A starts step t+2, the first to
+  // read them.
+  auto step = [&](auto has_next, auto parity, int t) {
+    constexpr int P = decltype(parity)::value;
+    matrix(has_next, parity);
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (!grp_a) prefetch(std::integral_constant<int, 1 - P>{}, t + 1);
+    if constexpr (decltype(has_next)::value) softmax(t + 1 == nfull, (t + 1) * BC);
+    __syncthreads();
+  };
+
+  if (!grp_a) {
+    fetch_k(0, 0, nfull == 0);
+    fetch_v(0, 0, nfull == 0);
+    if (tiles > 1) fetch_k(1, BC, nfull == 1);
+  }
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  qk(0, sc);
+  softmax(nfull == 0, 0);
+  __syncthreads();  // K stage 0 is free for tile 2
+  if (!grp_a) {     // group B starts half a step late
+    prefetch(std::integral_constant<int, 0>{}, 0);
+    __syncthreads();
+  }
+
   using T0 = std::integral_constant<int, 0>;
   using T1 = std::integral_constant<int, 1>;
   const std::true_type Y;
   const std::false_type N;
-
-  int j = 0;
-  for (; j + 2 < tiles; j += 2) {  // pairs of iterations that both have a next tile
-    iteration(Y, T0{}, j, sA, sB);
-    iteration(Y, T1{}, j + 1, sB, sA);
+  int t = 0;
+  for (; t + 2 < tiles; t += 2) {
+    step(Y, T0{}, t);
+    step(Y, T1{}, t + 1);
   }
-  // j is even here and the current scores are in sA.
-  if (j + 1 < tiles) {
-    iteration(Y, T0{}, j, sA, sB);
-    iteration(N, T1{}, j + 1, sB, sA);
+  if (t + 1 < tiles) {
+    step(Y, T0{}, t);
+    step(N, T1{}, t + 1);
   } else {
-    iteration(N, T0{}, j, sA, sB);
+    step(N, T0{}, t);
   }
-  if constexpr (kRowSumMfma) {
-    l = lacc[0];  // already the sum over both half-waves' keys
-  } else {        // add the partner half-wave's partial sum
+  if (grp_a) __syncthreads();  // matches group B's extra barrier
+  {  // add the partner half-wave's partial sum
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l), __float_as_uint(l),
                                                      false, false);
     l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
