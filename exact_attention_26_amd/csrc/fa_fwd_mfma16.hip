@@ -40,19 +40,19 @@
 //    Both read patterns are free of LDS bank conflicts.
 //  * Two LDS stages each for K and V, K one tile ahead of V.
 //  * O (fp32) lives in MFMA accumulators for the whole loop, one query per
-//    lane, so the rescale by alpha is a per-lane scalar multiply, skipped
-//    when no row's running max moved by more than FA_RESCALE_TAU.
+//    lane, so the rescale by alpha is a per-lane scalar multiply. It and the
+//    row max are skipped while the sums of p show that no p exceeds 2^8.
 #include <type_traits>
 
 #include "fa_device.h"
 
 // Build options (defaults are the shipped configuration):
 //   FA_RESCALE_TAU (8): the reference max m of the running sums moves (and
-//     O, l are rescaled by exp2((m_old - m_new) * c)) only when some row's
-//     max exceeds it by more than TAU in log2 units. O/l and L = m + ln l
-//     are the same for any reference, so this changes rounding only; p stays
-//     below 2^TAU (no overflow in fp32, bf16 or fp16). 0 rescales on every
-//     increase of the max.
+//     O, l are rescaled by exp2((m_old - m_new) * c)) only when some lane's
+//     sum of p over a tile exceeds 2^TAU; then m becomes the exact running
+//     max. O/l and L = m + ln l are the same for any reference, so this
+//     changes rounding only; every p stays at most 2^TAU (no overflow in
+//     fp32, bf16 or fp16).
 //   FA_PP_PRIO (1): s_setprio of a wave during its matrix half.
 //   FA_PP_AHEAD (2): MFMA steps between an LDS operand read and its use.
 #ifndef FA_RESCALE_TAU
@@ -300,21 +300,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
                                                      false, false);
     return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
   };
-  // p = exp2(s*c - m*c) in place; returns this lane's sum of p (VALU sums).
-  auto expo = [&](f32x16 (&s)[2], float mc) {
-    float ls[4];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[kt][i] = __builtin_amdgcn_exp2f(fmaf(s[kt][i], c2, -mc));
-        if (kt == 0 && i < 4)
-          ls[i] = s[kt][i];
-        else
-          ls[i & 3] += s[kt][i];
-      }
-    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
-  };
 
   const int nfull = n / BC;  // tiles with all BC keys valid
   const int tiles = (n + BC - 1) / BC;
@@ -333,33 +318,54 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
   float m = -INFINITY;  // running max of raw q.k (scale > 0)
   f32x16 sc[2];         // scores of the next tile
 
-  // Softmax half for the score tile in sc (keys kb..kb+63): row max, rescale
-  // of O and l when some row's max moved, exponentials, row sums, P packed.
+  // Softmax half for the score tile in sc (keys kb..kb+63), without a row
+  // max in the common case: p = exp2(s*c - m*c) against the current
+  // reference m, summed per lane. p >= 0, so a lane sum <= 2^FA_RESCALE_TAU
+  // bounds every p of that lane; when that holds in every lane, m stays.
+  // Otherwise (a score came near or above the bound; rare once m has
+  // settled) the row max is taken, O and l are rescaled to it exactly by
+  // alpha = exp2((m_old - m_new)*c), and p is recomputed from the scores,
+  // which are still in sc. On the first tile m = -inf, every lane sum is
+  // +inf (or NaN next to a masked key) and this exact path runs with
+  // alpha = 0. Then row sums, and P rounded and packed for P.V.
   auto softmax = [&](bool ragged, int kb) __attribute__((always_inline)) {
     if (ragged) mask(sc, kb);
-    const float mx = rowmax(sc);
-    if (__any((mx - m) * c2 > (float)FA_RESCALE_TAU)) {
-      const float mnew = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c2);  // 0 on the first tile
+    f32x16 pf[2];
+    auto exps = [&]() {
+      const float mc = m * c2;
+      float ls[4];
 #pragma unroll
-      for (int t = 0; t < D / 32; ++t)
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-      l *= alpha;
-      m = mnew;
+        for (int i = 0; i < 16; ++i) {
+          pf[kt][i] = __builtin_amdgcn_exp2f(fmaf(sc[kt][i], c2, -mc));
+          ls[i & 3] = (kt == 0 && i < 4) ? pf[kt][i] : ls[i & 3] + pf[kt][i];
+        }
+      return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+    };
+    float lsum = exps();
+    if (__any(!(lsum <= (float)(1u << FA_RESCALE_TAU)))) {
+      const float mx = rowmax(sc);
+      if (__any(mx > m)) {
+        const float mnew = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c2);
+#pragma unroll
+        for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+        l *= alpha;
+        m = mnew;
+        lsum = exps();
+      }
     }
-    // fp32 adds for the row sum (a packed bf16 dot2 would wait for the
-    // matrix pipe, which the partner wave keeps busy).
-    l += expo(sc, m * c2);
+    l += lsum;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       u32x4 pw;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        pw[q] = pack2<BF16>(sc[t >> 1][8 * (t & 1) + 2 * q], sc[t >> 1][8 * (t & 1) + 2 * q + 1]);
+        pw[q] = pack2<BF16>(pf[t >> 1][8 * (t & 1) + 2 * q], pf[t >> 1][8 * (t & 1) + 2 * q + 1]);
       pb[t] = __builtin_bit_cast(vec8, pw);
-      // Finish P here: without this the compiler sinks the exponentials past
-      // the barrier into the next matrix half, next to their use.
       __asm__ volatile("" : "+v"(pb[t]));
     }
     __asm__ volatile("" : "+v"(l));
