@@ -1,4 +1,4 @@
-"""Float64 CPU oracle for the attention forward (test infrastructure).
+"""Float64 CPU oracle for the attention forward and backward (test infrastructure).
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg may
 import this package. The HIP library never calls it and shares no code
@@ -15,4 +15,10 @@ from .attention_f64 import (  # noqa: F401
     attention_varlen_rows,
     attention_tiled,
     scores_to_weights,
+)
+from .attention_bwd_f64 import (  # noqa: F401
+    attention_backward,
+    attention_backward_lse,
+    attention_backward_dense,
+    row_dot,
 )

@@ -107,3 +107,77 @@ def test_unmodified_oracle_passes():
 @pytest.mark.parametrize("mutation", sorted(MUTATIONS))
 def test_planted_mistake_is_caught(mutation):
     assert not pins_pass(load_oracle(mutation))
+
+
+# ---------------------------------------------------------------------------
+# The backward oracle: the same scheme on oracle/attention_bwd_f64.py.
+# ---------------------------------------------------------------------------
+BWD_SRC = os.path.join(os.path.dirname(ORACLE_SRC), "attention_bwd_f64.py")
+
+BWD_MUTATIONS = {
+    "drop_D": ("dS = P * (dP - D)", "dS = P * dP"),
+    "wrong_D_sign": ("dS = P * (dP - D)", "dS = P * (dP + D)"),
+    "D_without_O": ("D = np.sum(dO[rows] * O, axis=1, keepdims=True)",
+                    "D = np.sum(dO[rows], axis=1, keepdims=True)"),
+    "dQ_without_scale": ("dQ[rows] = scale * (dS @ K)", "dQ[rows] = (dS @ K)"),
+    "dQ_against_V": ("dQ[rows] = scale * (dS @ K)", "dQ[rows] = scale * (dS @ V)"),
+    "dK_without_scale": ("dK += scale * (dS.T @ Q[rows])", "dK += (dS.T @ Q[rows])"),
+    "dK_against_dO": ("dK += scale * (dS.T @ Q[rows])", "dK += scale * (dS.T @ dO[rows])"),
+    "dV_from_P_times_dP": ("dV += P.T @ dO[rows]", "dV += (P * (dO[rows] @ V.T)).T @ dO[rows]"),
+    "P_unnormalised": ("P = E / E.sum(axis=1, keepdims=True)", "P = E"),
+    "normaliser_over_queries": ("P = E / E.sum(axis=1, keepdims=True)", "P = E / E.sum(axis=0, keepdims=True)"),
+    "no_max_shift_overflow": ("E = np.exp(S - S.max(axis=1, keepdims=True))", "E = np.exp(S)"),
+}
+
+
+def load_bwd(mutation=None):
+    """The backward oracle's module, with the mutation (if any) applied
+    inside attention_backward's body only (the same text also appears in the
+    docstring and in the rendering from L)."""
+    src = open(BWD_SRC).read()
+    if mutation is not None:
+        old, new = BWD_MUTATIONS[mutation]
+        a = src.index("def attention_backward(")
+        b = src.index("def attention_backward_lse(")
+        body = src[a:b]
+        assert body.count(old) == 1, f"mutation site for {mutation!r} not found exactly once"
+        src = src[:a] + body.replace(old, new) + src[b:]
+    mod = types.ModuleType("bwd_oracle_under_test")
+    exec(compile(src, BWD_SRC, "exec"), mod.__dict__)
+    return mod
+
+
+def bwd_pins_pass(mod) -> bool:
+    """The backward pin suite in miniature: torch autograd in float64 (a
+    library's own derivative), a large-score case and the key-sum identity."""
+    try:
+        with np.errstate(all="ignore"):
+            rng = np.random.default_rng(1)
+            for (n, m, d, scale) in [(7, 9, 4, 0.6), (12, 5, 4, 1.3), (3, 3, 4, 0.2)]:
+                Q, K, V, G = (rng.standard_normal(s) for s in ((n, d), (m, d), (m, d), (n, d)))
+                got = mod.attention_backward(Q, K, V, G, scale)
+                q, k, v = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+                o = torch.nn.functional.scaled_dot_product_attention(q[None], k[None], v[None],
+                                                                     scale=scale)[0]
+                o.backward(torch.tensor(G))
+                for a, b in zip(got, (q.grad, k.grad, v.grad)):
+                    if not (a.shape == b.shape and np.max(np.abs(a - b.numpy())) <= 1e-12):
+                        return False
+            # scores of several hundred: no overflow
+            Q = rng.standard_normal((4, 4)) * 30
+            K = rng.standard_normal((6, 4)) * 30
+            V, G = rng.standard_normal((6, 4)), rng.standard_normal((4, 4))
+            if not all(np.all(np.isfinite(g)) for g in mod.attention_backward(Q, K, V, G, 1.0)):
+                return False
+        return True
+    except Exception:
+        return False
+
+
+def test_unmodified_bwd_oracle_passes():
+    assert bwd_pins_pass(load_bwd(None))
+
+
+@pytest.mark.parametrize("mutation", sorted(BWD_MUTATIONS))
+def test_planted_bwd_mistake_is_caught(mutation):
+    assert not bwd_pins_pass(load_bwd(mutation))
