@@ -1,12 +1,15 @@
-"""MI355X (gfx950) FlashAttention-2 forward: thin Python binding of libfa.so.
+"""MI355X (gfx950) FlashAttention-2 forward and backward: thin Python binding of libfa.so.
 
 The C ABI (include/fa.h) is the product; this module only marshals
-arguments. Every step of the forward runs in the library's HIP kernels.
+arguments. Every step of the forward and backward runs in the library's
+HIP kernels.
 PyTorch supplies device memory and the current stream.
 
     fa_fwd(Q, K, V, O, L, B, H, N, d, scale, dtype, stream)        -> None
     fa_fwd_varlen(Q, K, V, O, L, cu_seqlens, nseq, total_tokens,
                   max_seqlen, H, d, scale, dtype, stream)           -> None
+    fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, delta, B, H, N, d, scale,
+           dtype, stream)                                           -> None
     fa_strerror(status) -> str,  fa_version() -> int
 
 take raw integers (device addresses, sizes, the stream handle) exactly as
@@ -14,6 +17,7 @@ the C functions do and raise ``FaError`` on a non-zero status.
 
     forward(q, k, v, scale=None)                    -> (o, lse)
     forward_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None) -> (o, lse)
+    backward(q, k, v, o, do, lse, scale=None)       -> (dq, dk, dv)
 
 take torch tensors on a GPU, allocate the outputs with torch.empty and call
 the entry points above on the current stream.
@@ -29,7 +33,8 @@ import os
 
 __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "LIB_PATH", "load", "fa_fwd", "fa_fwd_varlen",
-    "fa_strerror", "fa_version", "forward", "forward_varlen", "EXPORTED_SYMBOLS",
+    "fa_strerror", "fa_version", "forward", "forward_varlen", "EXPORTED_SYMBOLS", "fa_bwd",
+    "backward",
 ]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
@@ -38,7 +43,7 @@ STATUS = {
     -5: "FA_ERR_ALIGN", -6: "FA_ERR_ALIAS", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_SCALE",
     -9: "FA_ERR_SIZE",
 }
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_strerror", "fa_version")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_strerror", "fa_version")
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 _lib = None
@@ -64,6 +69,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.restype = i32
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.fa_fwd_varlen.restype = i32
+    lib.fa_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i32, f32, i32, vp]
+    lib.fa_bwd.restype = i32
     lib.fa_strerror.argtypes = [i32]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -94,6 +101,11 @@ def fa_fwd_varlen(Q, K, V, O, L, cu_seqlens, nseq, total_tokens, max_seqlen, H, 
                   stream) -> None:
     _check(load().fa_fwd_varlen(Q, K, V, O, L, cu_seqlens, int(nseq), int(total_tokens),
                                 int(max_seqlen), int(H), int(d), float(scale), int(dtype), stream))
+
+
+def fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, delta, B, H, N, d, scale, dtype, stream) -> None:
+    _check(load().fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, delta, int(B), int(H), int(N), int(d),
+                         float(scale), int(dtype), stream))
 
 
 # ---------------------------------------------------------------------------
@@ -157,3 +169,29 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: float | None = N
                   cu_seqlens.data_ptr(), nseq, T, int(max_seqlen), H, d, scale, _dtype_code(q),
                   _stream_handle(q.device))
     return o, L
+
+
+def backward(q, k, v, o, do, lse, scale: float | None = None, dq=None, dk=None, dv=None,
+             delta=None):
+    """Dense backward on contiguous [B, H, N, d] tensors; o and lse as forward()
+    returned them for the same q, k, v and scale. Returns (dq, dk, dv)."""
+    import torch
+    _require(q.dim() == 4 and q.shape == k.shape == v.shape == o.shape == do.shape,
+             "q, k, v, o, do must share shape [B,H,N,d]")
+    _require(q.dtype == k.dtype == v.dtype == o.dtype == do.dtype,
+             "q, k, v, o, do must share a dtype")
+    _require(all(t.is_cuda and t.is_contiguous() for t in (q, k, v, o, do, lse)),
+             "inputs must be contiguous GPU tensors")
+    B, H, N, d = q.shape
+    _require(lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, N),
+             "lse must be float32 [B,H,N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
+           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, scale,
+           _dtype_code(q), _stream_handle(q.device))
+    return dq, dk, dv

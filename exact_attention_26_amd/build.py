@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.hip", "fa_fwd_f32.hip", "fa_fwd_mfma16.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd_f32.hip", "fa_fwd_mfma16.hip", "fa_bwd.hip"]
 ARCH = "gfx950"
 
 

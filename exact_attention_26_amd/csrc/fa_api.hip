@@ -1,4 +1,4 @@
-// C-ABI entry points of the FlashAttention-2 forward library (include/fa.h):
+// C-ABI entry points of the FlashAttention-2 library (include/fa.h):
 // argument validation, work-grid sizing and dispatch to the gfx950 kernels.
 //
 // Validation touches no HIP API, so every error path returns before
@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 100;  // 0.1.0
+constexpr int kVersion = 200;  // 0.2.0: adds fa_bwd
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -140,13 +140,68 @@ int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L
   return launch(p, d, dtype, true, stream);
 }
 
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+           const float* L, void* dQ, void* dK, void* dV, float* delta, int B, int H, int N, int d,
+           float scale, int dtype, void* stream) {
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+
+  if ((int64_t)N * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
+  const int kb = (N + fa::kBwdKeysPerBlock - 1) / fa::kBwdKeysPerBlock;
+  const int qb = (N + fa::kBwdQueriesPerBlock - 1) / fa::kBwdQueriesPerBlock;
+  if ((int64_t)kb * H * B > kMaxBlocks || (int64_t)qb * H * B > kMaxBlocks) return FA_ERR_SIZE;
+  const int64_t rows = (int64_t)B * H * N;
+  if ((rows + 15) / 16 > kMaxBlocks) return FA_ERR_SIZE;  // the D kernel: >= 16 rows per block
+  if (!Q || !K || !V || !O || !dO || !L || !dQ || !dK || !dV || !delta) return FA_ERR_NULL;
+  const void* all[] = {Q, K, V, O, dO, L, dQ, dK, dV, delta};
+  for (const void* ptr : all)
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  const uint64_t tb = (uint64_t)rows * d * 2, rb = (uint64_t)rows * 4;
+  const void* in[] = {Q, K, V, O, dO, L};
+  const uint64_t in_b[] = {tb, tb, tb, tb, tb, rb};
+  const void* out[] = {dQ, dK, dV, delta};
+  const uint64_t out_b[] = {tb, tb, tb, rb};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(out[i], out_b[i], in[j], in_b[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(out[i], out_b[i], out[j], out_b[j])) return FA_ERR_ALIAS;
+  }
+
+  fa::BwdParams p{};
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.dout = dO;
+  p.lse = L;
+  p.dq = dQ;
+  p.dk = dK;
+  p.dv = dV;
+  p.delta = delta;
+  p.head_stride = (int64_t)N * d;
+  p.rows = rows;
+  p.BH = B * H;
+  p.N = N;
+  p.kblocks = kb;
+  p.qblocks = qb;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t e =
+      fa::launch_bwd(p, d, dtype == FA_BF16, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative or inconsistent sizes";
     case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension must be 64 or 128";
-    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype must be FA_F32, FA_F16 or FA_BF16";
+    case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype not supported by this entry point";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not suitably aligned";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or the other output";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime refused the kernel launch";

@@ -16,6 +16,53 @@ typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
 typedef _Float16 f16x8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
 
+// 16-bit MFMA operand types and helpers shared by the 16-bit kernels.
+template <bool BF16>
+struct Elem;
+template <>
+struct Elem<true> {
+  using vec8 = bf16x8;
+};
+template <>
+struct Elem<false> {
+  using vec8 = f16x8;
+};
+
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma32x32x16(typename Elem<BF16>::vec8 a,
+                                               typename Elem<BF16>::vec8 b, f32x16 c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Two fp32 values -> two 16-bit values of the storage dtype (round to
+// nearest even), packed low-first into one dword.
+template <bool BF16>
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+  if constexpr (BF16) {
+    typedef __bf16 v2 __attribute__((__vector_size__(2 * sizeof(__bf16))));
+    v2 r;
+    r[0] = (__bf16)a;
+    r[1] = (__bf16)b;
+    return __builtin_bit_cast(unsigned, r);
+  } else {
+    typedef _Float16 v2 __attribute__((__vector_size__(2 * sizeof(_Float16))));
+    v2 r;
+    r[0] = (_Float16)a;
+    r[1] = (_Float16)b;
+    return __builtin_bit_cast(unsigned, r);
+  }
+}
+
+
 // The chip has 8 XCDs, each with its own L2, and consecutive workgroup ids
 // are dealt to the XCDs round-robin. Work units that share K/V (the
 // Q-blocks of one head) get consecutive logical ids, so this mapping sends

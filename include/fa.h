@@ -1,5 +1,6 @@
 /*
- * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 forward library.
+ * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 library: forward
+ * (dense and packed variable-length) and dense backward.
  *
  * What is computed. For every (batch, head) -- or every (sequence, head)
  * in the packed variable-length entry -- and every query row r:
@@ -18,7 +19,8 @@
  * key/value head counts are equal.
  *
  * Conventions shared by every entry point:
- *   - Q, K, V, O, L and cu_seqlens are DEVICE pointers, allocated and owned
+ *   - Every tensor argument (Q, K, V, O, L, cu_seqlens, dO, dQ, dK, dV,
+ *     delta) is a DEVICE pointer, allocated and owned
  *     by the caller. The library allocates nothing, keeps no per-call state
  *     and never synchronises: work is enqueued on `stream` (a hipStream_t
  *     passed as void*; NULL = the default stream) and the caller
@@ -57,7 +59,7 @@ typedef enum {
   FA_ERR_NULL = -1,     /* a required pointer is NULL                        */
   FA_ERR_SHAPE = -2,    /* a negative size, or inconsistent varlen sizes     */
   FA_ERR_HEADDIM = -3,  /* d not in {64, 128}                                */
-  FA_ERR_DTYPE = -4,    /* dtype not an fa_dtype value                       */
+  FA_ERR_DTYPE = -4,    /* dtype not an fa_dtype value, or not supported     */
   FA_ERR_ALIGN = -5,    /* a pointer not 16-byte aligned                     */
   FA_ERR_ALIAS = -6,    /* an output overlaps an input or the other output   */
   FA_ERR_LAUNCH = -7,   /* the HIP runtime refused the kernel launch         */
@@ -97,6 +99,39 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
 int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L,
                   const int32_t* cu_seqlens, int nseq, int total_tokens, int max_seqlen,
                   int H, int d, float scale, int dtype, void* stream);
+
+/*
+ * Dense backward: the gradients of sum(O * dO) with respect to Q, K and V.
+ * "FlashAttention -- for programmers, not researchers", STAGE 5: the score
+ * tiles are recomputed from the forward's row statistic L rather than kept
+ * from the forward; the products are those of the backward list in the
+ * flash-attention documentation (S = Q K^T, dP = dO V^T, dV = P^T dO,
+ * dK = dS^T Q, dQ = dS K):
+ *
+ *     P[r, c]  = exp(S[r, c] - L[r])            (S as in the forward)
+ *     D[r]     = sum_k dO[r, k] * O[r, k]
+ *     dS[r, c] = P[r, c] * (sum_k dO[r, k] * V[c, k] - D[r])
+ *     dV = P^T dO,   dQ = scale * dS K,   dK = scale * dS^T Q
+ *
+ *   Q, K, V, O, dO : contiguous [B, H, N, d] tensors of `dtype`; O and L as
+ *                    fa_fwd wrote them for the same Q, K, V and scale.
+ *   L              : contiguous [B, H, N] float32, natural-log logsumexp.
+ *   dQ, dK, dV     : contiguous [B, H, N, d] tensors of `dtype`, written.
+ *   delta          : contiguous [B, H, N] float32 scratch owned by the
+ *                    caller; receives D. Its contents on entry are ignored.
+ *   dtype          : FA_F16 or FA_BF16 (FA_ERR_DTYPE otherwise: there is no
+ *                    fp32 backward).
+ * Arithmetic: products of dtype values summed in fp32; P and dS rounded to
+ * dtype (round to nearest even) as operands of the products that consume
+ * them; each gradient rounded to dtype once. Every output element is
+ * produced by one workgroup in a fixed order, so results are bitwise
+ * reproducible. All pointers 16-byte aligned (FA_ERR_ALIGN); dQ, dK, dV and
+ * delta must not overlap each other or any input (FA_ERR_ALIAS). Other
+ * checks and conventions as for fa_fwd. Returns an fa_status.
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+           const float* L, void* dQ, void* dK, void* dV, float* delta,
+           int B, int H, int N, int d, float scale, int dtype, void* stream);
 
 /* Static, NUL-terminated description of an fa_status value. */
 const char* fa_strerror(int status);

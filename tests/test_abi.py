@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert fa.fa_version() == 100
+    assert fa.fa_version() == 200
     for code, name in fa.STATUS.items():
         assert fa.fa_strerror(code).startswith(name)
     assert fa.fa_strerror(12345) == "unknown fa_status"
@@ -112,3 +112,37 @@ def test_binding_raises_named_error(lib):
     with pytest.raises(fa.FaError) as e:
         fa.fa_fwd(A, B_, C, D, E, 1, 1, 10, 48, 0.1, fa.FA_BF16, None)
     assert e.value.status == -3 and e.value.name == "FA_ERR_HEADDIM"
+
+
+# fa_bwd: ten buffers at distinct fake addresses.
+BW = {name: 0x10000000 * (i + 1) for i, name in
+      enumerate(("Q", "K", "V", "O", "dO", "L", "dQ", "dK", "dV", "delta"))}
+
+
+def bwd(lib, B=2, H=3, N=100, d=64, scale=0.125, dtype=fa.FA_BF16, **ptrs):
+    a = dict(BW, **ptrs)
+    return lib.fa_bwd(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["L"], a["dQ"], a["dK"], a["dV"],
+                      a["delta"], B, H, N, d, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=fa.FA_F32), -4), (dict(dtype=5), -4),
+    (dict(B=-1), -2), (dict(N=-3), -2), (dict(d=80), -3), (dict(scale=0.0), -8),
+    (dict(scale=float("nan")), -8), (dict(N=1 << 25, d=64), -9),
+    (dict(dO=0), -1), (dict(L=0), -1), (dict(dQ=0), -1), (dict(delta=0), -1),
+    (dict(dK=BW["dK"] + 8), -5), (dict(delta=BW["delta"] + 4), -5), (dict(O=BW["O"] + 2), -5),
+    (dict(dQ=BW["Q"]), -6), (dict(dV=BW["dO"] + 64), -6), (dict(dK=BW["dQ"]), -6),
+    (dict(delta=BW["L"]), -6), (dict(delta=BW["dV"] + 16), -6), (dict(dQ=BW["L"] - 32), -6),
+])
+def test_bwd_validation(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
+def test_bwd_empty_is_noop(lib, kw):
+    assert bwd(lib, **kw) == 0
+
+
+def test_bwd_inputs_may_alias_each_other(lib):
+    # shared inputs (Q == K == V) are legal; d = 96 then fails only the head-dim check
+    assert bwd(lib, K=BW["Q"], V=BW["Q"], d=96) == -3

@@ -96,6 +96,16 @@ def dense_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,
     return draw_qkv(rng, (B, H, N, d), dtype, qk_std, v_uniform)
 
 
+def dense_bwd_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,
+                     qk_std: float = 1.0, v_uniform: bool = False):
+    """Q, K, V as dense_inputs draws them, then the upstream gradient dO ~ N(0,1)
+    from the same generator; all [B,H,N,d] CPU tensors of `dtype`."""
+    rng = np.random.default_rng(seed)
+    q, k, v = draw_qkv(rng, (B, H, N, d), dtype, qk_std, v_uniform)
+    do = _round(rng.standard_normal((B, H, N, d), dtype=np.float32), dtype)
+    return q, k, v, do
+
+
 def varlen_lengths(nseq: int, lo: int, hi: int, seed: int = 0) -> np.ndarray:
     """Sequence lengths ~ U{lo..hi} (inclusive), the first draw of the seed."""
     rng = np.random.default_rng(seed)
