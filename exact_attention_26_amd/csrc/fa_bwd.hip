@@ -21,6 +21,8 @@
 //  3. dQ: a workgroup owns 128 queries (4 waves x 32) and streams the keys in
 //     tiles of 64, as the forward does: S^T = K Q^T and dP^T = V dO^T (Q and
 //     dO in VGPRs), P^T, dS^T, then dQ^T += K^T dS^T (K^T read transposed).
+//     Held to 2 waves per SIMD (<= 256 VGPRs), so each SIMD has a second
+//     wave to issue while one waits.
 // No atomics: each gradient element is produced by one workgroup in a fixed
 // order, so results are bitwise reproducible. The cost is that S and dP are
 // computed in both kernels (7 products instead of 5).
@@ -196,13 +198,25 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {  // 32-query halves of the tile
       f32x16 s = {}, dp = {};         // rows: query hq*32 + 8(i/4) + 4g + i%4; column: key l32
+      {
+        // Q and dO row operands read two k-steps ahead of their MFMAs.
+        constexpr int NS = D / 16;
+        vec8 qa[3], oa[3];
+        auto rd = [&](int ss) {
+          const int r = hq * 32 + l32, cb = (2 * ss + g) * 16;
+          qa[ss % 3] = *(const __attribute__((address_space(3))) vec8*)(Qs + T::off(r, cb));
+          oa[ss % 3] = *(const __attribute__((address_space(3))) vec8*)(Os + T::off(r, cb));
+        };
+        rd(0);
+        rd(1);
 #pragma unroll
-      for (int ss = 0; ss < D / 16; ++ss) {
-        const int r = hq * 32 + l32, cb = (2 * ss + g) * 16;
-        const vec8 qa = *(const __attribute__((address_space(3))) vec8*)(Qs + T::off(r, cb));
-        const vec8 oa = *(const __attribute__((address_space(3))) vec8*)(Os + T::off(r, cb));
-        s = mfma32x32x16<BF16>(qa, kf[ss], s);
-        dp = mfma32x32x16<BF16>(oa, vf[ss], dp);
+        for (int ss = 0; ss < NS; ++ss) {
+          if (ss + 2 < NS) rd(ss + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          s = mfma32x32x16<BF16>(qa[ss % 3], kf[ss], s);
+          dp = mfma32x32x16<BF16>(oa[ss % 3], vf[ss], dp);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       float pr[16], ds[16];
 #pragma unroll
@@ -233,25 +247,36 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
         pp[t] = __builtin_bit_cast(vec8, w1);
         pd[t] = __builtin_bit_cast(vec8, w2);
       }
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) {
-          i16x4 ho[2], hqv[2];
+      {
+        // dO^T and Q^T operands (transposed reads) two steps ahead of their MFMAs.
+        constexpr int NST = 2 * (D / 32);
+        i16x4 ho[3][2], hqv[3][2];
+        auto rd = [&](int k) {
+          const int t = k / (D / 32), dt = k % (D / 32);
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const int r = hq * 32 + 16 * t + 8 * h + vrow;
             const int o = T::off(r, 64 * dt + vin);
-            ho[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Os + o));
-            hqv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Qs + o));
+            ho[k % 3][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Os + o));
+            hqv[k % 3][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Qs + o));
           }
-          const i16x8 ao = {ho[0][0], ho[0][1], ho[0][2], ho[0][3],
-                            ho[1][0], ho[1][1], ho[1][2], ho[1][3]};
-          const i16x8 aq = {hqv[0][0], hqv[0][1], hqv[0][2], hqv[0][3],
-                            hqv[1][0], hqv[1][1], hqv[1][2], hqv[1][3]};
+        };
+        rd(0);
+        rd(1);
+#pragma unroll
+        for (int k = 0; k < NST; ++k) {
+          const int t = k / (D / 32), dt = k % (D / 32);
+          if (k + 2 < NST) rd(k + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          const i16x8 ao = {ho[k % 3][0][0], ho[k % 3][0][1], ho[k % 3][0][2], ho[k % 3][0][3],
+                            ho[k % 3][1][0], ho[k % 3][1][1], ho[k % 3][1][2], ho[k % 3][1][3]};
+          const i16x8 aq = {hqv[k % 3][0][0], hqv[k % 3][0][1], hqv[k % 3][0][2], hqv[k % 3][0][3],
+                            hqv[k % 3][1][0], hqv[k % 3][1][1], hqv[k % 3][1][2], hqv[k % 3][1][3]};
           dv[dt] = mfma32x32x16<BF16>(__builtin_bit_cast(vec8, ao), pp[t], dv[dt]);
           dk[dt] = mfma32x32x16<BF16>(__builtin_bit_cast(vec8, aq), pd[t], dk[dt]);
+          __builtin_amdgcn_sched_barrier(0);
         }
+      }
     }
   };
 
@@ -288,7 +313,7 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
 // 3. dQ: one workgroup per (head, 128 queries).
 // ---------------------------------------------------------------------------
 template <bool BF16, int D>
-__global__ __launch_bounds__(kThreadsB) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2))) void bwd_dq_kernel(BwdParams p) {
   using vec8 = typename Elem<BF16>::vec8;
   using T = BTile<D>;
   constexpr int STG = 2 * T::TILEB;  // K tile, V tile
