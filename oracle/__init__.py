@@ -22,3 +22,9 @@ from .attention_bwd_f64 import (  # noqa: F401
     attention_backward_dense,
     row_dot,
 )
+from .attention_band_f64 import (  # noqa: F401
+    attention_banded,
+    attention_banded_rows,
+    attention_banded_dense,
+    attention_banded_dense_rows,
+)

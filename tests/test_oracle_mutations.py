@@ -181,3 +181,99 @@ def test_unmodified_bwd_oracle_passes():
 @pytest.mark.parametrize("mutation", sorted(BWD_MUTATIONS))
 def test_planted_bwd_mistake_is_caught(mutation):
     assert not bwd_pins_pass(load_bwd(mutation))
+
+
+# ---------------------------------------------------------------------------
+# The banded oracle: the same scheme on oracle/attention_band_f64.py.
+# ---------------------------------------------------------------------------
+BAND_SRC = os.path.join(os.path.dirname(ORACLE_SRC), "attention_band_f64.py")
+
+BAND_MUTATIONS = {
+    "edge_excluded": ("<= window   #", "< window   #"),
+    "one_sided": ("np.abs(sel[:, None] - keys[None, :]) <= window",
+                  "(keys[None, :] - sel[:, None]) <= window"),
+    "chunk_local_row_index": ("np.abs(sel[:, None] - keys[None, :])",
+                              "np.abs(np.arange(sel.size)[:, None] - keys[None, :])"),
+    "masked_score_zero": ("np.where(band, scale * (Q[sel] @ K.T), -np.inf)",
+                          "np.where(band, scale * (Q[sel] @ K.T), 0.0)"),
+    "drop_scale": ("np.where(band, scale * (Q[sel] @ K.T), -np.inf)",
+                   "np.where(band, (Q[sel] @ K.T), -np.inf)"),
+    "mask_ignored": ("np.where(band, scale * (Q[sel] @ K.T), -np.inf)",
+                     "np.where(True, scale * (Q[sel] @ K.T), -np.inf)"),
+    "drop_max_in_L": ("L[s:s + sel.size] = m[:, 0] + np.log(l[:, 0])",
+                      "L[s:s + sel.size] = np.log(l[:, 0])"),
+    "drop_normaliser": ("O[s:s + sel.size] = (P / l) @ V", "O[s:s + sel.size] = P @ V"),
+}
+
+
+def load_band(mutation=None):
+    src = open(BAND_SRC).read()
+    if mutation is not None:
+        old, new = BAND_MUTATIONS[mutation]
+        a = src.index("def attention_banded_rows(")
+        b = src.index("def attention_banded(")
+        body = src[a:b]
+        assert body.count(old) == 1, f"mutation site for {mutation!r} not found exactly once"
+        src = src[:a] + body.replace(old, new) + src[b:]
+    mod = types.ModuleType("band_oracle_under_test")
+    exec(compile(src, BAND_SRC, "exec"), mod.__dict__)
+    return mod
+
+
+def _brute_band(Q, K, V, scale, w, rows):
+    mpmath.mp.dps = 50
+    O = np.zeros((len(rows), V.shape[1]))
+    L = np.zeros(len(rows))
+    for i, r in enumerate(rows):
+        cs = [c for c in range(K.shape[0]) if abs(r - c) <= w]
+        s = {c: mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(Q[r, t]) * mpmath.mpf(K[c, t])
+                                                for t in range(Q.shape[1])) for c in cs}
+        z = mpmath.fsum(mpmath.exp(s[c]) for c in cs)
+        L[i] = float(mpmath.log(z))
+        for j in range(V.shape[1]):
+            O[i, j] = float(mpmath.fsum(mpmath.exp(s[c]) * mpmath.mpf(V[c, j]) for c in cs) / z)
+    return O, L
+
+
+def band_pins_pass(mod) -> bool:
+    """The banded pin suite in miniature: brute force over the in-band keys
+    (whole heads and a row subset), torch attention with a boolean mask and
+    the identical-keys band mean."""
+    try:
+        with np.errstate(all="ignore"):
+            rng = np.random.default_rng(2)
+            for (n, d, w, rows) in [(6, 3, 0, None), (9, 4, 2, None), (5, 2, 9, None),
+                                    (12, 3, 2, [4, 9])]:
+                Q, K, V = (rng.standard_normal((n, d)) for _ in range(3))
+                O, L = mod.attention_banded_rows(Q, K, V, 0.8, w, rows)
+                Ob, Lb = _brute_band(Q, K, V, 0.8, w, range(n) if rows is None else rows)
+                if not (np.max(np.abs(O - Ob)) <= 1e-13 and np.max(np.abs(L - Lb)) <= 1e-13):
+                    return False
+            Q, K, V = (rng.standard_normal((100, 16)) for _ in range(3))
+            O, _ = mod.attention_banded(Q, K, V, 0.25, 7)
+            idx = torch.arange(100)
+            allowed = (idx[:, None] - idx[None, :]).abs() <= 7
+            t = lambda a: torch.from_numpy(a)[None, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(t(Q), t(K), t(V),
+                                                                   attn_mask=allowed, scale=0.25)
+            if not np.max(np.abs(O - ref[0, 0].numpy())) <= 1e-12:
+                return False
+            k = rng.standard_normal(16)
+            O, L = mod.attention_banded(Q[:40], np.tile(k, (40, 1)), V[:40], 0.6, 3)
+            for r in range(40):
+                lo, hi = max(0, r - 3), min(39, r + 3)
+                if not (np.max(np.abs(O[r] - V[lo:hi + 1].mean(axis=0))) <= 1e-13
+                        and abs(L[r] - (0.6 * Q[r] @ k + math.log(hi - lo + 1))) <= 1e-13):
+                    return False
+        return True
+    except Exception:
+        return False
+
+
+def test_unmodified_band_oracle_passes():
+    assert band_pins_pass(load_band(None))
+
+
+@pytest.mark.parametrize("mutation", sorted(BAND_MUTATIONS))
+def test_planted_band_mistake_is_caught(mutation):
+    assert not band_pins_pass(load_band(mutation))
