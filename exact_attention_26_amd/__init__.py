@@ -1,4 +1,4 @@
-"""MI355X (gfx950) FlashAttention-2 forward and backward: thin Python binding of libfa.so.
+"""MI355X (gfx950) FlashAttention-2 forward (full and banded) and backward: thin Python binding of libfa.so.
 
 The C ABI (include/fa.h) is the product; this module only marshals
 arguments. Every step of the forward and backward runs in the library's
@@ -8,6 +8,8 @@ PyTorch supplies device memory and the current stream.
     fa_fwd(Q, K, V, O, L, B, H, N, d, scale, dtype, stream)        -> None
     fa_fwd_varlen(Q, K, V, O, L, cu_seqlens, nseq, total_tokens,
                   max_seqlen, H, d, scale, dtype, stream)           -> None
+    fa_fwd_banded(Q, K, V, O, L, B, H, N, d, window, scale, dtype,
+                  stream)                                           -> None
     fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, delta, B, H, N, d, scale,
            dtype, stream)                                           -> None
     fa_strerror(status) -> str,  fa_version() -> int
@@ -17,6 +19,7 @@ the C functions do and raise ``FaError`` on a non-zero status.
 
     forward(q, k, v, scale=None)                    -> (o, lse)
     forward_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None) -> (o, lse)
+    forward_banded(q, k, v, window, scale=None)     -> (o, lse)
     backward(q, k, v, o, do, lse, scale=None)       -> (dq, dk, dv)
 
 take torch tensors on a GPU, allocate the outputs with torch.empty and call
@@ -34,7 +37,7 @@ import os
 __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "LIB_PATH", "load", "fa_fwd", "fa_fwd_varlen",
     "fa_strerror", "fa_version", "forward", "forward_varlen", "EXPORTED_SYMBOLS", "fa_bwd",
-    "backward",
+    "backward", "fa_fwd_banded", "forward_banded",
 ]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
@@ -43,7 +46,8 @@ STATUS = {
     -5: "FA_ERR_ALIGN", -6: "FA_ERR_ALIAS", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_SCALE",
     -9: "FA_ERR_SIZE",
 }
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_bwd", "fa_strerror", "fa_version")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_banded", "fa_bwd", "fa_strerror",
+                    "fa_version")
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 _lib = None
@@ -69,6 +73,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd.restype = i32
     lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.fa_fwd_varlen.restype = i32
+    lib.fa_fwd_banded.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.fa_fwd_banded.restype = i32
     lib.fa_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i32, f32, i32, vp]
     lib.fa_bwd.restype = i32
     lib.fa_strerror.argtypes = [i32]
@@ -101,6 +107,11 @@ def fa_fwd_varlen(Q, K, V, O, L, cu_seqlens, nseq, total_tokens, max_seqlen, H, 
                   stream) -> None:
     _check(load().fa_fwd_varlen(Q, K, V, O, L, cu_seqlens, int(nseq), int(total_tokens),
                                 int(max_seqlen), int(H), int(d), float(scale), int(dtype), stream))
+
+
+def fa_fwd_banded(Q, K, V, O, L, B, H, N, d, window, scale, dtype, stream) -> None:
+    _check(load().fa_fwd_banded(Q, K, V, O, L, int(B), int(H), int(N), int(d), int(window),
+                                float(scale), int(dtype), stream))
 
 
 def fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, delta, B, H, N, d, scale, dtype, stream) -> None:
@@ -144,6 +155,25 @@ def forward(q, k, v, scale: float | None = None, out=None, lse=None):
     L = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), L.data_ptr(), B, H, N, d,
            scale, _dtype_code(q), _stream_handle(q.device))
+    return o, L
+
+
+def forward_banded(q, k, v, window: int, scale: float | None = None, out=None, lse=None):
+    """Dense banded forward on contiguous [B, H, N, d] fp16/bf16 tensors: row r
+    attends to keys c with |r - c| <= window. Returns (o, lse[B,H,N] fp32)."""
+    import torch
+    _require(q.dim() == 4 and q.shape == k.shape == v.shape, "q, k, v must share shape [B,H,N,d]")
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    _require(q.is_cuda and k.is_cuda and v.is_cuda, "q, k, v must be GPU tensors")
+    _require(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(),
+             "q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    L = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    fa_fwd_banded(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), L.data_ptr(), B, H, N,
+                  d, window, scale, _dtype_code(q), _stream_handle(q.device))
     return o, L
 
 

@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 200;  // 0.2.0: adds fa_bwd
+constexpr int kVersion = 300;  // 0.3.0: adds fa_fwd_banded
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -93,6 +93,43 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B
   p.q_blocks = (N + br - 1) / br;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.window = -1;
+  return launch(p, d, dtype, false, stream);
+}
+
+int fa_fwd_banded(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H,
+                  int N, int d, int window, float scale, int dtype, void* stream) {
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 0 || H < 0 || N < 0 || window < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+
+  if ((int64_t)N * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
+  const int br = fa::kRowsPerBlock16;
+  if ((int64_t)((N + br - 1) / br) * H * B > kMaxBlocks) return FA_ERR_SIZE;
+  const uint64_t elems = (uint64_t)B * H * N * d;
+  const int st = check_buffers(Q, K, V, O, L, elems * 2, (uint64_t)B * H * N * 4);
+  if (st != FA_OK) return st;
+
+  fa::FwdParams p{};
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.lse = L;
+  p.cu_seqlens = nullptr;
+  p.batch_stride = (int64_t)H * N * d;
+  p.head_stride = (int64_t)N * d;
+  p.row_stride = d;
+  p.B = B;
+  p.H = H;
+  p.N = N;
+  p.total_tokens = 0;
+  p.q_blocks = (N + br - 1) / br;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.window = window < N ? window : N;  // a window of N or more keeps every key
   return launch(p, d, dtype, false, stream);
 }
 
@@ -137,6 +174,7 @@ int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L
   p.q_blocks = (max_seqlen + br - 1) / br;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
+  p.window = -1;
   return launch(p, d, dtype, true, stream);
 }
 
@@ -199,7 +237,7 @@ const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
-    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative or inconsistent sizes";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: negative or inconsistent sizes or window";
     case FA_ERR_HEADDIM: return "FA_ERR_HEADDIM: head dimension must be 64 or 128";
     case FA_ERR_DTYPE: return "FA_ERR_DTYPE: dtype not supported by this entry point";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not suitably aligned";

@@ -32,6 +32,8 @@ struct FwdParams {
   int q_blocks;               // ceil(N / rows per workgroup)
   float scale;                // softmax scale applied to q.k
   float scale_log2;           // scale * log2(e): exp(x*scale) = exp2(x*scale_log2)
+  int window;                 // banded (dense 16-bit only): row r sees keys |r - c| <= window,
+                              // 0 <= window <= N; -1 = every key
 };
 
 // One backward problem (dense [B,H,N,d]), already validated on the host.

@@ -90,7 +90,12 @@ struct Tile {
   __device__ static int vswz(int r) { return (r / ROWS_PER_256) & (VCHUNKS - 1); }
 };
 
-template <bool BF16, int D, bool VARLEN>
+// BAND: row r only attends to keys c with |r - c| <= p.window (local
+// window; "FlashAttention -- for programmers, not researchers", DEMO 6). The
+// workgroup visits only the key tiles that hold a key within the window of
+// one of its rows, and masks per element only in the tiles where the band
+// edge cuts a wave's 32 x 64 block.
+template <bool BF16, int D, bool VARLEN, bool BAND>
 __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
   using vec8 = typename Elem<BF16>::vec8;
   using T = Tile<D>;
@@ -121,11 +126,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
     if (qrow < n) w = *(const u32x4*)(Qg + qrow * rs + 16 * s + 8 * g);
     qf[s] = __builtin_bit_cast(vec8, w);
   }
-  // Consume Q here so the compiler waits for these loads before the key
-  // loop; otherwise it places that wait inside the loop, where it would
-  // also stall on the prefetch of the next K/V tile.
-#pragma unroll
-  for (int s = 0; s < D / 16; ++s) __asm__ volatile("" : : "v"(qf[s]));
 
   // LDS holds two K stages followed by two V stages. K runs one tile ahead
   // of V: while tile j's P.V reads V stage j%2, the S^T of tile j+1 reads K
@@ -231,14 +231,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
         s[kt] = mfma32x32x16<BF16>(a, qf[ss], s[kt]);
       }
   };
-  // Keys >= n of the tile at kb score -inf (probability 0).
+  // Keys >= n of the tile at kb (and, with a band, keys farther than the
+  // window from this lane's query row) score -inf (probability 0).
+  const int win = BAND ? p.window : 0;
   auto mask = [&](f32x16 (&s)[2], int kb) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = kb + kt * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (key >= n) s[kt][i] = -INFINITY;
+        bool out = key >= n;
+        if constexpr (BAND) out = out || (unsigned)(key - qrow + win) > (unsigned)(2 * win);
+        if (out) s[kt][i] = -INFINITY;
       }
   };
   // Max over this lane's 32 scores, then over the partner lane l ^ 32
@@ -257,7 +261,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
   };
 
   const int nfull = n / BC;  // tiles with all BC keys valid
-  const int tiles = (n + BC - 1) / BC;
+  // Key tiles visited: t0 .. t0 + tiles - 1. With a band, only those that
+  // hold a key within the window of one of the workgroup's rows (whole
+  // tiles outside are skipped; the host caps the window at n).
+  int t0 = 0, tiles = (n + BC - 1) / BC;
+  if constexpr (BAND) {
+    const int lo = max(0, u.q0 - win);
+    const int hi = min(n - 1, min(u.q0 + BR, n) - 1 + win);
+    t0 = lo / BC;
+    tiles = hi / BC - t0 + 1;
+  }
+  const int rag = nfull - t0;  // visiting index of the ragged tile, if any
+  // With a band, whether the edge of the band cuts this wave's block of 32
+  // query rows x the 64 keys at kb (then the tile is masked per element).
+  const int row0 = u.q0 + wave * 32;
+  auto band_edge = [&](int kb) {
+    return BAND && (kb + BC - 1 - row0 > win || row0 + 31 - kb > win);
+  };
 
   static_assert(kWaves == 8, "ping-pong pairs waves w and w+4 on one SIMD");
   // Ping-pong: waves 0-3 (group A) and 4-7 (group B) share the four SIMDs,
@@ -270,7 +290,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
   // far better than MFMAs and exponentials issued by one wave.
   const bool grp_a = wave < 4;
   vec8 pb[4];           // P of the current tile, storage dtype: P.V B operands
-  float m = -INFINITY;  // running max of raw q.k (scale > 0)
+  // Running max of raw q.k (scale > 0). With a band it starts at a large
+  // finite negative value instead of -inf: a row may meet whole tiles with
+  // every key masked before its first in-band key, and exp2(-inf*c - m*c)
+  // must then be 0, not NaN. The first in-band key moves m and rescales by
+  // exp2((-1e30 - m)*c) = 0, so nothing from before survives.
+  float m = BAND ? -1e30f : -INFINITY;
   f32x16 sc[2];         // scores of the next tile
 
   // Softmax half for the score tile in sc (keys kb..kb+63), without a row
@@ -284,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
   // +inf (or NaN next to a masked key) and this exact path runs with
   // alpha = 0. Then row sums, and P rounded and packed for P.V.
   auto softmax = [&](bool ragged, int kb) __attribute__((always_inline)) {
-    if (ragged) mask(sc, kb);
+    if (ragged || band_edge(kb)) mask(sc, kb);
     f32x16 pf[2];
     auto exps = [&]() {
       const float mc = m * c2;
@@ -376,8 +401,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
   // 1-P (it held V of tile t-1, last read in step t-1).
   auto prefetch = [&](auto parity, int t) {
     constexpr int P = decltype(parity)::value;
-    if (t + 2 < tiles) fetch_k(P, (t + 2) * BC, t + 2 == nfull);
-    if (t + 1 < tiles) fetch_v(1 - P, (t + 1) * BC, t + 1 == nfull);
+    if (t + 2 < tiles) fetch_k(P, (t0 + t + 2) * BC, t + 2 == rag);
+    if (t + 1 < tiles) fetch_v(1 - P, (t0 + t + 1) * BC, t + 1 == rag);
   };
   // Step t: [matrix(t)] | [softmax of tile t+1] |. Group B runs every step
   // one half-step (one barrier) after group A, so on each SIMD the matrix
@@ -392,19 +417,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (!grp_a) prefetch(std::integral_constant<int, 1 - P>{}, t + 1);
-    if constexpr (decltype(has_next)::value) softmax(t + 1 == nfull, (t + 1) * BC);
+    if constexpr (decltype(has_next)::value) softmax(t + 1 == rag, (t0 + t + 1) * BC);
     __syncthreads();
   };
 
   if (!grp_a) {
-    fetch_k(0, 0, nfull == 0);
-    fetch_v(0, 0, nfull == 0);
-    if (tiles > 1) fetch_k(1, BC, nfull == 1);
+    fetch_k(0, t0 * BC, rag == 0);
+    fetch_v(0, t0 * BC, rag == 0);
+    if (tiles > 1) fetch_k(1, (t0 + 1) * BC, rag == 1);
   }
+  // Consume Q here, after the first copies are issued, so its load latency
+  // overlaps theirs and the compiler waits for these loads before the key
+  // loop; otherwise it places that wait inside the loop, where it would
+  // also stall on the prefetch of the next K/V tile.
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) __asm__ volatile("" : : "v"(qf[s]));
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   qk(0, sc);
-  softmax(nfull == 0, 0);
+  softmax(rag == 0, t0 * BC);
   __syncthreads();  // K stage 0 is free for tile 2
   if (!grp_a) {     // group B starts half a step late
     prefetch(std::integral_constant<int, 0>{}, 0);
@@ -451,20 +482,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
 }
 
 template <bool BF16, int D>
-const void* pick(bool varlen) {
-  return varlen ? (const void*)fwd16_kernel<BF16, D, true>
-                : (const void*)fwd16_kernel<BF16, D, false>;
+const void* pick(bool varlen, bool band) {
+  if (band) return (const void*)fwd16_kernel<BF16, D, false, true>;
+  return varlen ? (const void*)fwd16_kernel<BF16, D, true, false>
+                : (const void*)fwd16_kernel<BF16, D, false, false>;
 }
 
 }  // namespace
 
 hipError_t launch_fwd_mfma16(const FwdParams& p, int d, bool bf16, bool varlen,
                              hipStream_t stream) {
+  const bool band = p.window >= 0;
   const void* fn = nullptr;
   if (bf16)
-    fn = (d == 64) ? pick<true, 64>(varlen) : pick<true, 128>(varlen);
+    fn = (d == 64) ? pick<true, 64>(varlen, band) : pick<true, 128>(varlen, band);
   else
-    fn = (d == 64) ? pick<false, 64>(varlen) : pick<false, 128>(varlen);
+    fn = (d == 64) ? pick<false, 64>(varlen, band) : pick<false, 128>(varlen, band);
   const dim3 grid((unsigned)((int64_t)p.q_blocks * p.H * p.B));
   const dim3 block(kThreads);
   FwdParams arg = p;

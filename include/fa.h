@@ -1,6 +1,6 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 library: forward
- * (dense and packed variable-length) and dense backward.
+ * (dense, packed variable-length and dense banded) and dense backward.
  *
  * What is computed. For every (batch, head) -- or every (sequence, head)
  * in the packed variable-length entry -- and every query row r:
@@ -16,7 +16,8 @@
  * j = 0"). It is the same function as plain softmax attention, not an
  * approximation ("FlashAttention -- for programmers, not researchers",
  * STAGE 4 and DEMO 6). No causal mask, no dropout, no bias; query and
- * key/value head counts are equal.
+ * key/value head counts are equal. fa_fwd_banded restricts every row to a
+ * local window of keys.
  *
  * Conventions shared by every entry point:
  *   - Every tensor argument (Q, K, V, O, L, cu_seqlens, dO, dQ, dK, dV,
@@ -57,7 +58,7 @@ typedef enum {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,     /* a required pointer is NULL                        */
-  FA_ERR_SHAPE = -2,    /* a negative size, or inconsistent varlen sizes     */
+  FA_ERR_SHAPE = -2,    /* a negative size or window, or inconsistent sizes  */
   FA_ERR_HEADDIM = -3,  /* d not in {64, 128}                                */
   FA_ERR_DTYPE = -4,    /* dtype not an fa_dtype value, or not supported     */
   FA_ERR_ALIGN = -5,    /* a pointer not 16-byte aligned                     */
@@ -99,6 +100,29 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
 int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L,
                   const int32_t* cu_seqlens, int nseq, int total_tokens, int max_seqlen,
                   int H, int d, float scale, int dtype, void* stream);
+
+/*
+ * Dense banded (local-window) forward: as fa_fwd, except that query row r
+ * only attends to the keys c with |r - c| <= window; the scores of all other
+ * keys count as -inf before the row softmax:
+ *
+ *     S[r, c] = scale * dot(Q[r, :], K[c, :])   if |r - c| <= window, else -inf
+ *     O, L    as for fa_fwd, over the kept keys only
+ *
+ * "FlashAttention -- for programmers, not researchers", DEMO 6, where the
+ * local window (64 there) is the contrast to exact attention: a different
+ * function. The key of a row's own index is always kept, so every O and L
+ * is finite. Work grows with the window, not with N: a workgroup reads only
+ * the key tiles that reach its rows' windows.
+ *   Q, K, V, O, L : as for fa_fwd ([B, H, N, d] and [B, H, N]).
+ *   window        : >= 0 (FA_ERR_SHAPE otherwise); window >= N - 1 keeps
+ *                   every key and computes the same function as fa_fwd.
+ *   dtype         : FA_F16 or FA_BF16 (FA_ERR_DTYPE otherwise).
+ * Other checks and conventions as for fa_fwd. Returns an fa_status.
+ */
+int fa_fwd_banded(const void* Q, const void* K, const void* V, void* O, float* L,
+                  int B, int H, int N, int d, int window, float scale, int dtype,
+                  void* stream);
 
 /*
  * Dense backward: the gradients of sum(O * dO) with respect to Q, K and V.

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert fa.fa_version() == 200
+    assert fa.fa_version() == 300
     for code, name in fa.STATUS.items():
         assert fa.fa_strerror(code).startswith(name)
     assert fa.fa_strerror(12345) == "unknown fa_status"
@@ -146,3 +146,25 @@ def test_bwd_empty_is_noop(lib, kw):
 def test_bwd_inputs_may_alias_each_other(lib):
     # shared inputs (Q == K == V) are legal; d = 96 then fails only the head-dim check
     assert bwd(lib, K=BW["Q"], V=BW["Q"], d=96) == -3
+
+
+def banded(lib, Q=A, K=B_, V=C, O=D, L=E, B=2, H=3, N=100, d=64, window=16, scale=0.125,
+           dtype=fa.FA_BF16):
+    return lib.fa_fwd_banded(Q, K, V, O, L, B, H, N, d, window, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=fa.FA_F32), -4), (dict(dtype=3), -4),
+    (dict(window=-1), -2), (dict(window=-(1 << 30)), -2), (dict(B=-1), -2), (dict(N=-2), -2),
+    (dict(d=32), -3), (dict(scale=0.0), -8), (dict(scale=float("inf")), -8),
+    (dict(N=1 << 25, d=64), -9),
+    (dict(Q=0), -1), (dict(L=0), -1), (dict(K=B_ + 8), -5), (dict(L=E + 4), -5),
+    (dict(O=A), -6), (dict(L=D + 16), -6),
+])
+def test_banded_validation(lib, kw, status):
+    assert banded(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=0, window=1 << 30)])
+def test_banded_empty_is_noop(lib, kw):
+    assert banded(lib, **kw) == 0

@@ -159,3 +159,15 @@ def attention_flops(B: int, H: int, N: int, d: int) -> int:
 
 def varlen_flops(lengths, H: int, d: int) -> int:
     return 4 * H * d * int(sum(int(n) * int(n) for n in lengths))
+
+
+def band_pairs(N: int, window: int) -> int:
+    """Number of (query, key) pairs with |r - c| <= window among N x N."""
+    if window >= N - 1:
+        return N * N
+    return N * (2 * window + 1) - window * (window + 1)
+
+
+def banded_flops(B: int, H: int, N: int, d: int, window: int) -> int:
+    """Counted work of one banded forward: 4 d flops per in-band pair."""
+    return 4 * B * H * d * band_pairs(N, window)
