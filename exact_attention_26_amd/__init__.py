@@ -10,6 +10,8 @@ PyTorch supplies device memory and the current stream.
                   max_seqlen, H, d, scale, dtype, stream)           -> None
     fa_fwd_banded(Q, K, V, O, L, B, H, N, d, window, scale, dtype,
                   stream)                                           -> None
+    fa_fwd_kv_outer(Q, K, V, O, L, acc, B, H, N, d, q_groups, scale,
+                    dtype, stream)                                  -> None
     fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, delta, B, H, N, d, scale,
            dtype, stream)                                           -> None
     fa_strerror(status) -> str,  fa_version() -> int
@@ -20,6 +22,7 @@ the C functions do and raise ``FaError`` on a non-zero status.
     forward(q, k, v, scale=None)                    -> (o, lse)
     forward_varlen(q, k, v, cu_seqlens, max_seqlen, scale=None) -> (o, lse)
     forward_banded(q, k, v, window, scale=None)     -> (o, lse)
+    forward_kv_outer(q, k, v, q_groups, scale=None) -> (o, lse)
     backward(q, k, v, o, do, lse, scale=None)       -> (dq, dk, dv)
 
 take torch tensors on a GPU, allocate the outputs with torch.empty and call
@@ -37,7 +40,7 @@ import os
 __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "LIB_PATH", "load", "fa_fwd", "fa_fwd_varlen",
     "fa_strerror", "fa_version", "forward", "forward_varlen", "EXPORTED_SYMBOLS", "fa_bwd",
-    "backward", "fa_fwd_banded", "forward_banded",
+    "backward", "fa_fwd_banded", "forward_banded", "fa_fwd_kv_outer", "forward_kv_outer",
 ]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
@@ -46,8 +49,8 @@ STATUS = {
     -5: "FA_ERR_ALIGN", -6: "FA_ERR_ALIAS", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_SCALE",
     -9: "FA_ERR_SIZE",
 }
-EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_banded", "fa_bwd", "fa_strerror",
-                    "fa_version")
+EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_banded", "fa_fwd_kv_outer", "fa_bwd",
+                    "fa_strerror", "fa_version")
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 _lib = None
@@ -75,6 +78,8 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_varlen.restype = i32
     lib.fa_fwd_banded.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.fa_fwd_banded.restype = i32
+    lib.fa_fwd_kv_outer.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.fa_fwd_kv_outer.restype = i32
     lib.fa_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i32, f32, i32, vp]
     lib.fa_bwd.restype = i32
     lib.fa_strerror.argtypes = [i32]
@@ -112,6 +117,11 @@ def fa_fwd_varlen(Q, K, V, O, L, cu_seqlens, nseq, total_tokens, max_seqlen, H, 
 def fa_fwd_banded(Q, K, V, O, L, B, H, N, d, window, scale, dtype, stream) -> None:
     _check(load().fa_fwd_banded(Q, K, V, O, L, int(B), int(H), int(N), int(d), int(window),
                                 float(scale), int(dtype), stream))
+
+
+def fa_fwd_kv_outer(Q, K, V, O, L, acc, B, H, N, d, q_groups, scale, dtype, stream) -> None:
+    _check(load().fa_fwd_kv_outer(Q, K, V, O, L, acc, int(B), int(H), int(N), int(d),
+                                  int(q_groups), float(scale), int(dtype), stream))
 
 
 def fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, delta, B, H, N, d, scale, dtype, stream) -> None:
@@ -174,6 +184,30 @@ def forward_banded(q, k, v, window: int, scale: float | None = None, out=None, l
     L = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
     fa_fwd_banded(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), L.data_ptr(), B, H, N,
                   d, window, scale, _dtype_code(q), _stream_handle(q.device))
+    return o, L
+
+
+def forward_kv_outer(q, k, v, q_groups: int = 16, scale: float | None = None, out=None,
+                     lse=None, acc=None):
+    """Dense forward in the K/V-outer order on contiguous [B, H, N, d] fp16/bf16
+    tensors (same O and L as forward()); acc is the fp32 scratch of
+    B*H*N*(d+2) floats. Returns (o, lse[B,H,N] fp32)."""
+    import torch
+    _require(q.dim() == 4 and q.shape == k.shape == v.shape, "q, k, v must share shape [B,H,N,d]")
+    _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    _require(q.is_cuda and k.is_cuda and v.is_cuda, "q, k, v must be GPU tensors")
+    _require(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(),
+             "q, k, v must be contiguous")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    o = torch.empty_like(q) if out is None else out
+    L = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if acc is None:
+        acc = torch.empty(B * H * N * (d + 2), dtype=torch.float32, device=q.device)
+    fa_fwd_kv_outer(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), L.data_ptr(),
+                    acc.data_ptr(), B, H, N, d, q_groups, scale, _dtype_code(q),
+                    _stream_handle(q.device))
     return o, L
 
 

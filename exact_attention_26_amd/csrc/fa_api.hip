@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 300;  // 0.3.0: adds fa_fwd_banded
+constexpr int kVersion = 400;  // 0.4.0: adds fa_fwd_kv_outer
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -176,6 +176,59 @@ int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L
   p.scale_log2 = scale * 1.4426950408889634f;
   p.window = -1;
   return launch(p, d, dtype, true, stream);
+}
+
+int fa_fwd_kv_outer(const void* Q, const void* K, const void* V, void* O, float* L, float* acc,
+                    int B, int H, int N, int d, int q_groups, float scale, int dtype,
+                    void* stream) {
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 0 || H < 0 || N < 0 || q_groups < 1) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (B == 0 || H == 0 || N == 0) return FA_OK;
+
+  if ((int64_t)N * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
+  const int blocks32 = (N + 31) / 32;
+  const int groups_req = q_groups < blocks32 ? q_groups : blocks32;
+  const int rows = (blocks32 + groups_req - 1) / groups_req * 32;
+  const int groups = (N + rows - 1) / rows;  // non-empty groups only
+  if ((int64_t)groups * H * B > kMaxBlocks) return FA_ERR_SIZE;
+  if (!Q || !K || !V || !O || !L || !acc) return FA_ERR_NULL;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(L) ||
+      !aligned16(acc))
+    return FA_ERR_ALIGN;
+  const uint64_t rows_all = (uint64_t)B * H * N;
+  const uint64_t tb = rows_all * d * 2, lb = rows_all * 4, ab = rows_all * (d + 2) * 4;
+  const void* in[3] = {Q, K, V};
+  const void* out[3] = {O, L, acc};
+  const uint64_t out_b[3] = {tb, lb, ab};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 3; ++j)
+      if (overlap(out[i], out_b[i], in[j], tb)) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(out[i], out_b[i], out[j], out_b[j])) return FA_ERR_ALIAS;
+  }
+
+  fa::KvOuterParams p{};
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.lse = L;
+  p.oacc = acc;
+  p.mstat = acc + rows_all * d;
+  p.lstat = acc + rows_all * (d + 1);
+  p.head_stride = (int64_t)N * d;
+  p.BH = B * H;
+  p.N = N;
+  p.groups = groups;
+  p.rows_per_group = rows;
+  p.tiles = (N + 63) / 64;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const hipError_t e =
+      fa::launch_fwd_kv_outer(p, d, dtype == FA_BF16, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,

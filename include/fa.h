@@ -1,6 +1,7 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 library: forward
- * (dense, packed variable-length and dense banded) and dense backward.
+ * (dense, packed variable-length and dense banded), dense backward, and the
+ * K/V-outer forward used to measure the other loop order's traffic.
  *
  * What is computed. For every (batch, head) -- or every (sequence, head)
  * in the packed variable-length entry -- and every query row r:
@@ -123,6 +124,31 @@ int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L
 int fa_fwd_banded(const void* Q, const void* K, const void* V, void* O, float* L,
                   int B, int H, int N, int d, int window, float scale, int dtype,
                   void* stream);
+
+/*
+ * Dense forward in the K/V-outer loop order (the traffic experiment): the
+ * same O and L as fa_fwd, computed with the key/value tiles (64 keys) on the
+ * outer loop. For every tile, each query row reads Q and reads back its
+ * running output O (fp32) and statistics m, l from `acc`, applies the
+ * online-softmax update, and writes them back; the last tile writes O / l
+ * and L = m + ln l instead. "Kernel visualization: Flash Attention 2",
+ * "Counting trips across HBM", explains why the Q-outer order of fa_fwd
+ * never makes those round trips; this entry point exists to measure them.
+ *   Q, K, V, O, L : as for fa_fwd ([B, H, N, d] and [B, H, N]).
+ *   acc           : float32 scratch owned by the caller, B*H*N*(d + 2)
+ *                   floats: the running O [B, H, N, d], then m [B, H, N],
+ *                   then l [B, H, N]. Contents on entry are ignored; on
+ *                   return they hold the state before the last tile.
+ *   q_groups      : >= 1 (FA_ERR_SHAPE otherwise): workgroups that split
+ *                   the query rows of one (batch, head); each streams all
+ *                   of that head's K/V tiles. Capped at ceil(N / 32).
+ *   dtype         : FA_F16 or FA_BF16 (FA_ERR_DTYPE otherwise).
+ * All pointers 16-byte aligned; O, L and acc must not overlap each other or
+ * Q, K, V (FA_ERR_ALIAS). Other checks as for fa_fwd. Returns an fa_status.
+ */
+int fa_fwd_kv_outer(const void* Q, const void* K, const void* V, void* O, float* L, float* acc,
+                    int B, int H, int N, int d, int q_groups, float scale, int dtype,
+                    void* stream);
 
 /*
  * Dense backward: the gradients of sum(O * dO) with respect to Q, K and V.

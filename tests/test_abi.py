@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert fa.fa_version() == 300
+    assert fa.fa_version() == 400
     for code, name in fa.STATUS.items():
         assert fa.fa_strerror(code).startswith(name)
     assert fa.fa_strerror(12345) == "unknown fa_status"
@@ -168,3 +168,31 @@ def test_banded_validation(lib, kw, status):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=0, window=1 << 30)])
 def test_banded_empty_is_noop(lib, kw):
     assert banded(lib, **kw) == 0
+
+
+# fa_fwd_kv_outer: six buffers at distinct fake addresses.
+KV = {name: 0x10000000 * (i + 1) for i, name in enumerate(("Q", "K", "V", "O", "L", "acc"))}
+
+
+def kv_outer(lib, B=2, H=3, N=100, d=64, groups=4, scale=0.125, dtype=fa.FA_BF16, **ptrs):
+    a = dict(KV, **ptrs)
+    return lib.fa_fwd_kv_outer(a["Q"], a["K"], a["V"], a["O"], a["L"], a["acc"], B, H, N, d,
+                               groups, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=fa.FA_F32), -4), (dict(dtype=9), -4),
+    (dict(groups=0), -2), (dict(groups=-3), -2), (dict(B=-1), -2), (dict(N=-1), -2),
+    (dict(d=96), -3), (dict(scale=0.0), -8), (dict(N=1 << 25, d=64), -9),
+    (dict(Q=0), -1), (dict(acc=0), -1), (dict(L=0), -1),
+    (dict(acc=KV["acc"] + 4), -5), (dict(O=KV["O"] + 8), -5),
+    (dict(acc=KV["Q"]), -6), (dict(acc=KV["O"] - 64), -6), (dict(L=KV["acc"] + 16), -6),
+    (dict(O=KV["V"] + 32), -6),
+])
+def test_kv_outer_validation(lib, kw, status):
+    assert kv_outer(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=0, groups=0 + 1)])
+def test_kv_outer_empty_is_noop(lib, kw):
+    assert kv_outer(lib, **kw) == 0

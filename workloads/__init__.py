@@ -171,3 +171,36 @@ def band_pairs(N: int, window: int) -> int:
 def banded_flops(B: int, H: int, N: int, d: int, window: int) -> int:
     """Counted work of one banded forward: 4 d flops per in-band pair."""
     return 4 * B * H * d * band_pairs(N, window)
+
+
+def traffic_q_outer(n: int, d: int, Br: int, elem: int, stat: int = 4) -> dict:
+    """Bytes one head moves between HBM and on-chip memory in the Q-outer
+    (FlashAttention-2) order, counted by the trip rules of "Kernel
+    visualization: Flash Attention 2" ("Counting trips across HBM") and the
+    move() accounting of "FlashAttention -- for programmers, not
+    researchers" (STAGE 4): Q read once, K and V read once per block of Br
+    query rows, O and L written once. Returns {tensor: (read, written)}."""
+    Tr = -(-n // Br)
+    return {"Q": (n * d * elem, 0), "K": (Tr * n * d * elem, 0), "V": (Tr * n * d * elem, 0),
+            "O": (0, n * d * elem), "L": (0, n * stat)}
+
+
+def traffic_kv_outer(n: int, d: int, Bc: int, elem: int, groups: int = 1, acc: int = 4,
+                     stat: int = 4) -> dict:
+    """The same for the K/V-outer order: the key/value tiles are the outer
+    loop (read once per group of query rows that streams them), and for
+    every tile each query row reads Q, and reads back and rewrites its
+    running output O (acc bytes per element) and its statistics m, l, which
+    therefore cross HBM once per key tile; the last tile writes the final O
+    (elem bytes) and L instead. Returns {tensor: (read, written)}."""
+    Tc = -(-n // Bc)
+    trips = Tc - 1
+    return {"Q": (Tc * n * d * elem, 0), "K": (groups * n * d * elem, 0),
+            "V": (groups * n * d * elem, 0), "O_acc": (trips * n * d * acc, trips * n * d * acc),
+            "m_l": (trips * 2 * n * stat, trips * 2 * n * stat), "O": (0, n * d * elem),
+            "L": (0, n * stat)}
+
+
+def traffic_total(t: dict) -> tuple:
+    """(bytes read, bytes written) of a traffic dict."""
+    return sum(r for r, _ in t.values()), sum(w for _, w in t.values())
