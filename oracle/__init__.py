@@ -28,3 +28,9 @@ from .attention_band_f64 import (  # noqa: F401
     attention_banded_dense,
     attention_banded_dense_rows,
 )
+from .dropout_add_norm_f64 import (  # noqa: F401
+    philox4x32_10,
+    keep_threshold,
+    dropout_keep,
+    dropout_add_norm,
+)

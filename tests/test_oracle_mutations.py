@@ -277,3 +277,95 @@ def test_unmodified_band_oracle_passes():
 @pytest.mark.parametrize("mutation", sorted(BAND_MUTATIONS))
 def test_planted_band_mistake_is_caught(mutation):
     assert not band_pins_pass(load_band(mutation))
+
+
+# ---------------------------------------------------------------------------
+# The dropout + residual + norm oracle: the same scheme on
+# oracle/dropout_add_norm_f64.py.
+# ---------------------------------------------------------------------------
+NORM_SRC = os.path.join(os.path.dirname(ORACLE_SRC), "dropout_add_norm_f64.py")
+
+NORM_MUTATIONS = {
+    "philox_multiplier": ("m0, m1 = np.uint64(0xD2511F53)", "m0, m1 = np.uint64(0xD2511F55)"),
+    "philox_nine_rounds": ("for r in range(10):", "for r in range(9):"),
+    "philox_no_key_bump": ("k0 = (k0 + w0) & _M32", "k0 = k0 & _M32"),
+    "philox_swapped_halves": ("c = [((p1 >> np.uint64(32)) ^ c[1] ^ k0) & _M32, p1 & _M32,",
+                              "c = [((p1 >> np.uint64(32)) ^ c[1] ^ k0) & _M32, p0 & _M32,"),
+    "word_index_shifted": ("word = words[np.arange(e.size), (e % np.uint64(4)).astype(np.int64)]",
+                           "word = words[np.arange(e.size), ((e + np.uint64(1)) % np.uint64(4)).astype(np.int64)]"),
+    "stream_ignored": ("+ stream) & 0xFFFFFFFF)", "+ 0) & 0xFFFFFFFF)"),
+    "no_keep_scale": ("z = np.where(keep0, x0 * keep_scale, 0.0)", "z = np.where(keep0, x0, 0.0)"),
+    "residual_dropped": ("z = z + _f64(residual)", "z = z + 0.0"),
+    "var_without_mean": ("var = np.mean((z - mean[:, None]) ** 2, axis=1)",
+                         "var = np.mean(z ** 2, axis=1)"),
+    "eps_outside_sqrt": ("rstd = 1.0 / np.sqrt(var + eps)", "rstd = 1.0 / np.sqrt(var) + eps"),
+    "rms_centred": ("zn = z * rstd[:, None]", "zn = (z - z.mean(axis=1, keepdims=True)) * rstd[:, None]"),
+    "beta_ignored": ("return y if b is None else y + _f64(b)[None, :]", "return y"),
+}
+
+
+def load_norm(mutation=None):
+    src = open(NORM_SRC).read()
+    if mutation is not None:
+        old, new = NORM_MUTATIONS[mutation]
+        a = src.index("def philox4x32_10(")
+        body = src[a:]
+        assert body.count(old) == 1, f"mutation site for {mutation!r} not found exactly once"
+        src = src[:a] + body.replace(old, new)
+    mod = types.ModuleType("norm_oracle_under_test")
+    exec(compile(src, NORM_SRC, "exec"), mod.__dict__)
+    return mod
+
+
+def norm_pins_pass(mod) -> bool:
+    """The norm pin suite in miniature: the generator's known answers, the
+    element-to-word order, torch's layer_norm and rms_norm in float64, the
+    exact keep scale and the parallel-residual sum with distinct streams."""
+    try:
+        with np.errstate(all="ignore"):
+            kat = [((0, 0, 0, 0), (0, 0), (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+                   ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+                    (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1))]
+            for ctr, key, want in kat:
+                got = mod.philox4x32_10(np.array([ctr], dtype=np.uint64), key)[0]
+                if tuple(int(x) for x in got) != want:
+                    return False
+            k = mod.dropout_keep(2, 16, 0.5, 3, 9, stream=1)
+            for e in range(32):
+                w = mod.philox4x32_10(np.array([[e // 4, 0, 9, 1]], dtype=np.uint64), (3, 0))
+                if k.reshape(-1)[e] != (int(w[0, e % 4]) >= 2**31):
+                    return False
+            rng = np.random.default_rng(3)
+            x0, x1, r = (rng.standard_normal((7, 64)) for _ in range(3))
+            g, b = 1 + 0.1 * rng.standard_normal(64), 0.1 * rng.standard_normal(64)
+            out = mod.dropout_add_norm(x0, g, b, residual=r, p=0.3, seed=4, offset=1)
+            s = 1 / (1 - np.float32(0.3).item())
+            z = np.where(out["keep0"], x0 * s, 0.0) + r
+            if not np.max(np.abs(out["z"] - z)) <= 1e-13:
+                return False
+            ref = torch.nn.functional.layer_norm(torch.from_numpy(z), (64,), torch.from_numpy(g),
+                                                 torch.from_numpy(b), eps=1e-5)
+            if not np.max(np.abs(out["y0"] - ref.numpy())) <= 1e-12:
+                return False
+            out = mod.dropout_add_norm(x0, g, None, residual=r, p=0.0, rms=True, eps=1e-6)
+            ref = torch.nn.functional.rms_norm(torch.from_numpy(x0 + r), (64,),
+                                               torch.from_numpy(g), eps=1e-6)
+            if not np.max(np.abs(out["y0"] - ref.numpy())) <= 1e-12:
+                return False
+            out = mod.dropout_add_norm(x0, g, b, residual=r, x1=x1, p=0.3, seed=2, offset=8)
+            z = (np.where(out["keep0"], x0 * s, 0.0) + np.where(out["keep1"], x1 * s, 0.0) + r)
+            if not (np.max(np.abs(out["z"] - z)) <= 1e-13
+                    and (out["keep0"] != out["keep1"]).mean() > 0.2):
+                return False
+        return True
+    except Exception:
+        return False
+
+
+def test_unmodified_norm_oracle_passes():
+    assert norm_pins_pass(load_norm(None))
+
+
+@pytest.mark.parametrize("mutation", sorted(NORM_MUTATIONS))
+def test_planted_norm_mistake_is_caught(mutation):
+    assert not norm_pins_pass(load_norm(mutation))
