@@ -1,4 +1,5 @@
-"""MI355X (gfx950) FlashAttention-2 forward (full and banded) and backward: thin Python binding of libfa.so.
+"""MI355X (gfx950) FlashAttention-2 forward (full and banded) and backward, and the fused
+dropout + residual + LayerNorm/RMSNorm op: thin Python binding of libfa.so.
 
 The C ABI (include/fa.h) is the product; this module only marshals
 arguments. Every step of the forward and backward runs in the library's
@@ -14,6 +15,10 @@ PyTorch supplies device memory and the current stream.
                     dtype, stream)                                  -> None
     fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, delta, B, H, N, d, scale,
            dtype, stream)                                           -> None
+    fa_dropout_add_norm(x0, x1, residual, gamma0, beta0, gamma1, beta1,
+                        y0, y1, z, mean, rstd, mask, rows, hidden,
+                        dropout_p, seed, offset, eps, norm, dtype,
+                        stream)                                     -> None
     fa_strerror(status) -> str,  fa_version() -> int
 
 take raw integers (device addresses, sizes, the stream handle) exactly as
@@ -24,6 +29,7 @@ the C functions do and raise ``FaError`` on a non-zero status.
     forward_banded(q, k, v, window, scale=None)     -> (o, lse)
     forward_kv_outer(q, k, v, q_groups, scale=None) -> (o, lse)
     backward(q, k, v, o, do, lse, scale=None)       -> (dq, dk, dv)
+    dropout_add_norm(x0, gamma0, ...)               -> dict of outputs
 
 take torch tensors on a GPU, allocate the outputs with torch.empty and call
 the entry points above on the current stream.
@@ -41,16 +47,18 @@ __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "LIB_PATH", "load", "fa_fwd", "fa_fwd_varlen",
     "fa_strerror", "fa_version", "forward", "forward_varlen", "EXPORTED_SYMBOLS", "fa_bwd",
     "backward", "fa_fwd_banded", "forward_banded", "fa_fwd_kv_outer", "forward_kv_outer",
+    "fa_dropout_add_norm", "dropout_add_norm", "FA_NORM_LAYER", "FA_NORM_RMS",
 ]
 
 FA_F32, FA_F16, FA_BF16 = 0, 1, 2
+FA_NORM_LAYER, FA_NORM_RMS = 0, 1
 STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_HEADDIM", -4: "FA_ERR_DTYPE",
     -5: "FA_ERR_ALIGN", -6: "FA_ERR_ALIAS", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_SCALE",
-    -9: "FA_ERR_SIZE",
+    -9: "FA_ERR_SIZE", -10: "FA_ERR_ARG",
 }
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_banded", "fa_fwd_kv_outer", "fa_bwd",
-                    "fa_strerror", "fa_version")
+                    "fa_dropout_add_norm", "fa_strerror", "fa_version")
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 _lib = None
@@ -80,6 +88,9 @@ def load() -> ctypes.CDLL:
     lib.fa_fwd_banded.restype = i32
     lib.fa_fwd_kv_outer.argtypes = [vp] * 6 + [i32, i32, i32, i32, i32, f32, i32, vp]
     lib.fa_fwd_kv_outer.restype = i32
+    u64 = ctypes.c_uint64
+    lib.fa_dropout_add_norm.argtypes = ([vp] * 13 + [i32, i32, f32, u64, u64, f32, i32, i32, vp])
+    lib.fa_dropout_add_norm.restype = i32
     lib.fa_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i32, f32, i32, vp]
     lib.fa_bwd.restype = i32
     lib.fa_strerror.argtypes = [i32]
@@ -122,6 +133,15 @@ def fa_fwd_banded(Q, K, V, O, L, B, H, N, d, window, scale, dtype, stream) -> No
 def fa_fwd_kv_outer(Q, K, V, O, L, acc, B, H, N, d, q_groups, scale, dtype, stream) -> None:
     _check(load().fa_fwd_kv_outer(Q, K, V, O, L, acc, int(B), int(H), int(N), int(d),
                                   int(q_groups), float(scale), int(dtype), stream))
+
+
+def fa_dropout_add_norm(x0, x1, residual, gamma0, beta0, gamma1, beta1, y0, y1, z, mean, rstd,
+                        mask, rows, hidden, dropout_p, seed, offset, eps, norm, dtype,
+                        stream) -> None:
+    _check(load().fa_dropout_add_norm(x0, x1, residual, gamma0, beta0, gamma1, beta1, y0, y1, z,
+                                      mean, rstd, mask, int(rows), int(hidden), float(dropout_p),
+                                      int(seed), int(offset), float(eps), int(norm), int(dtype),
+                                      stream))
 
 
 def fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, delta, B, H, N, d, scale, dtype, stream) -> None:
@@ -259,3 +279,48 @@ def backward(q, k, v, o, do, lse, scale: float | None = None, dq=None, dk=None, 
            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, scale,
            _dtype_code(q), _stream_handle(q.device))
     return dq, dk, dv
+
+
+def dropout_add_norm(x0, gamma0, beta0=None, residual=None, x1=None, gamma1=None, beta1=None,
+                     p: float = 0.0, seed: int = 0, offset: int = 0, eps: float = 1e-5,
+                     rms: bool = False, prenorm: bool = True, stats: bool = True,
+                     return_mask: bool = False, out=None):
+    """Fused dropout + residual + LayerNorm/RMSNorm on contiguous [rows, hidden]
+    fp16/bf16 GPU tensors (any leading shape is flattened into rows). Returns a
+    dict: y0, y1 (None without gamma1), z (None unless prenorm), mean (LayerNorm
+    only) and rstd (None unless stats), mask (uint8, None unless return_mask).
+    `out` may be a dict returned by an earlier call with the same arguments:
+    its tensors are written again instead of allocating new ones."""
+    import torch
+    hidden = x0.shape[-1]
+    rows = x0.numel() // hidden if hidden else 0
+    ts = [t for t in (x0, x1, residual) if t is not None]
+    ws = [t for t in (gamma0, beta0, gamma1, beta1) if t is not None]
+    _require(all(t.shape == x0.shape for t in ts), "x0, x1, residual must share a shape")
+    _require(all(t.numel() == hidden for t in ws), "gamma/beta must have `hidden` elements")
+    _require(all(t.dtype == x0.dtype for t in ts + ws), "all tensors must share a dtype")
+    _require(all(t.is_cuda and t.is_contiguous() for t in ts + ws),
+             "inputs must be contiguous GPU tensors")
+    if out is not None:
+        o = out
+        fa_dropout_add_norm(*(None if t is None else t.data_ptr() for t in
+                              (x0, x1, residual, gamma0, beta0, gamma1, beta1, o["y0"], o["y1"],
+                               o["z"], o["mean"], o["rstd"], o["mask"])),
+                            rows, hidden, p, seed, offset, eps,
+                            FA_NORM_RMS if rms else FA_NORM_LAYER, _dtype_code(x0),
+                            _stream_handle(x0.device))
+        return out
+    y0 = torch.empty_like(x0)
+    y1 = torch.empty_like(x0) if gamma1 is not None else None
+    z = torch.empty_like(x0) if prenorm else None
+    dev = x0.device
+    mean = torch.empty(rows, dtype=torch.float32, device=dev) if stats and not rms else None
+    rstd = torch.empty(rows, dtype=torch.float32, device=dev) if stats else None
+    mask = (torch.empty((2 if x1 is not None else 1, rows, hidden), dtype=torch.uint8, device=dev)
+            if return_mask else None)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    fa_dropout_add_norm(ptr(x0), ptr(x1), ptr(residual), ptr(gamma0), ptr(beta0), ptr(gamma1),
+                        ptr(beta1), ptr(y0), ptr(y1), ptr(z), ptr(mean), ptr(rstd), ptr(mask),
+                        rows, hidden, p, seed, offset, eps, FA_NORM_RMS if rms else FA_NORM_LAYER,
+                        _dtype_code(x0), _stream_handle(dev))
+    return {"y0": y0, "y1": y1, "z": z, "mean": mean, "rstd": rstd, "mask": mask}

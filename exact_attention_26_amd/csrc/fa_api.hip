@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int kVersion = 400;  // 0.4.0: adds fa_fwd_kv_outer
+constexpr int kVersion = 500;  // 0.5.0: adds fa_dropout_add_norm
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -231,6 +231,68 @@ int fa_fwd_kv_outer(const void* Q, const void* K, const void* V, void* O, float*
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int fa_dropout_add_norm(const void* x0, const void* x1, const void* residual, const void* gamma0,
+                        const void* beta0, const void* gamma1, const void* beta1, void* y0,
+                        void* y1, void* z, float* mean, float* rstd, unsigned char* mask,
+                        int rows, int hidden, float dropout_p, uint64_t seed, uint64_t offset,
+                        float eps, int norm, int dtype, void* stream) {
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (rows < 0 || hidden < 0 || hidden % 8 != 0 || hidden > 8192) return FA_ERR_SHAPE;
+  if (norm != FA_NORM_LAYER && norm != FA_NORM_RMS) return FA_ERR_ARG;
+  if (!(dropout_p >= 0.f && dropout_p < 1.f)) return FA_ERR_ARG;
+  if (!(eps > 0.f) || !isfinite(eps)) return FA_ERR_ARG;
+  if (rows == 0 || hidden == 0) return FA_OK;
+  if (rows > kMaxBlocks) return FA_ERR_SIZE;
+  if (!x0 || !gamma0 || !y0) return FA_ERR_NULL;
+  if ((gamma1 == nullptr) != (y1 == nullptr) || (beta1 && !gamma1)) return FA_ERR_NULL;
+  const void* t16[] = {x0, x1, residual, gamma0, beta0, gamma1, beta1, y0, y1, z, mask};
+  for (const void* t : t16)
+    if (t && !aligned16(t)) return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(mean) & 3u) || (reinterpret_cast<uintptr_t>(rstd) & 3u))
+    return FA_ERR_ALIGN;
+  const uint64_t rb = (uint64_t)rows * hidden * 2, wb = (uint64_t)hidden * 2;
+  const void* in[] = {x0, x1, residual, gamma0, beta0, gamma1, beta1};
+  const uint64_t in_b[] = {rb, rb, rb, wb, wb, wb, wb};
+  const void* out[] = {y0, y1, z, mean, rstd, mask};
+  const uint64_t out_b[] = {rb, rb, rb, (uint64_t)rows * 4, (uint64_t)rows * 4,
+                            (uint64_t)rows * hidden * (x1 ? 2 : 1)};
+  for (int i = 0; i < 6; ++i) {
+    if (!out[i]) continue;
+    for (int j = 0; j < 7; ++j)
+      if (in[j] && overlap(out[i], out_b[i], in[j], in_b[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 6; ++j)
+      if (out[j] && overlap(out[i], out_b[i], out[j], out_b[j])) return FA_ERR_ALIAS;
+  }
+
+  fa::NormParams p{};
+  p.x0 = x0;
+  p.x1 = x1;
+  p.res = residual;
+  p.g0 = gamma0;
+  p.b0 = beta0;
+  p.g1 = gamma1;
+  p.b1 = beta1;
+  p.y0 = y0;
+  p.y1 = y1;
+  p.z = z;
+  p.mean = mean;
+  p.rstd = rstd;
+  p.mask = mask;
+  p.rows = rows;
+  p.hidden = hidden;
+  p.thr = (uint32_t)floor((double)dropout_p * 4294967296.0);
+  p.keep_scale = 1.f / (1.f - dropout_p);
+  p.key0 = (uint32_t)seed;
+  p.key1 = (uint32_t)(seed >> 32);
+  p.ctr2 = (uint32_t)offset;
+  p.ctr3 = (uint32_t)(offset >> 32);
+  p.eps = eps;
+  p.rms = norm == FA_NORM_RMS;
+  const hipError_t e =
+      fa::launch_dropout_add_norm(p, dtype == FA_BF16, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
            const float* L, void* dQ, void* dK, void* dV, float* delta, int B, int H, int N, int d,
            float scale, int dtype, void* stream) {
@@ -298,6 +360,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime refused the kernel launch";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
     case FA_ERR_SIZE: return "FA_ERR_SIZE: tensor too large for 32-bit in-head offsets";
+    case FA_ERR_ARG: return "FA_ERR_ARG: an argument outside its documented range";
     default: return "unknown fa_status";
   }
 }

@@ -1,7 +1,8 @@
 /*
  * fa.h -- C ABI of the MI355X (gfx950) FlashAttention-2 library: forward
- * (dense, packed variable-length and dense banded), dense backward, and the
- * K/V-outer forward used to measure the other loop order's traffic.
+ * (dense, packed variable-length and dense banded), dense backward, the
+ * K/V-outer forward used to measure the other loop order's traffic, and the
+ * fused dropout + residual + LayerNorm/RMSNorm op.
  *
  * What is computed. For every (batch, head) -- or every (sequence, head)
  * in the packed variable-length entry -- and every query row r:
@@ -66,8 +67,14 @@ typedef enum {
   FA_ERR_ALIAS = -6,    /* an output overlaps an input or the other output   */
   FA_ERR_LAUNCH = -7,   /* the HIP runtime refused the kernel launch         */
   FA_ERR_SCALE = -8,    /* scale not finite or not > 0                       */
-  FA_ERR_SIZE = -9      /* a tensor too large for 32-bit in-head offsets     */
+  FA_ERR_SIZE = -9,     /* a tensor too large for 32-bit in-head offsets     */
+  FA_ERR_ARG = -10      /* an argument outside its documented range          */
 } fa_status;
+
+typedef enum {
+  FA_NORM_LAYER = 0,    /* LayerNorm: (z - mean) / sqrt(var + eps)           */
+  FA_NORM_RMS = 1       /* RMSNorm:   z / sqrt(mean(z^2) + eps)              */
+} fa_norm;
 
 /*
  * Dense forward.
@@ -149,6 +156,51 @@ int fa_fwd_banded(const void* Q, const void* K, const void* V, void* O, float* L
 int fa_fwd_kv_outer(const void* Q, const void* K, const void* V, void* O, float* L, float* acc,
                     int B, int H, int N, int d, int q_groups, float scale, int dtype,
                     void* stream);
+
+/*
+ * Fused dropout + residual add + LayerNorm / RMSNorm over rows of `hidden`
+ * values: the fused op of flash-attention's documentation (the paragraph on
+ * its dropout / residual / LayerNorm extension: pre- and post-norm, RMSNorm,
+ * parallel residuals, hidden up to 8192 in multiples of 8). Per row:
+ *
+ *     z  = dropout(x0) + dropout(x1) + residual
+ *     y0 = norm(z) * gamma0 + beta0,    y1 = norm(z) * gamma1 + beta1
+ *     FA_NORM_LAYER: norm(z) = (z - mean) * rstd, rstd = 1/sqrt(var + eps)
+ *     FA_NORM_RMS:   norm(z) = z * rstd,          rstd = 1/sqrt(mean(z^2) + eps)
+ *
+ * Dropout: element e = row*hidden + col of branch s (0 for x0, 1 for x1) is
+ * kept when word e % 4 of Philox4x32-10 (Salmon et al., SC'11) at counter
+ * (e / 4 mod 2^32, e / 4 div 2^32, offset mod 2^32, offset div 2^32 + s),
+ * key (seed mod 2^32, seed div 2^32), is >= floor(dropout_p * 2^32); kept
+ * values are multiplied by 1 / (1 - dropout_p) (fp32). dropout_p = 0 keeps
+ * every element without drawing.
+ *   x0            : [rows, hidden] of `dtype`; required.
+ *   x1, residual  : [rows, hidden] or NULL (no parallel branch / no residual).
+ *   gamma0, beta0 : [hidden] of `dtype`; gamma0 required, beta0 NULL = 0.
+ *   gamma1, beta1 : second weight set or NULL; y1 is written iff gamma1 is
+ *                   given (then y1 must be non-NULL, and beta1 needs gamma1).
+ *   y0, y1        : [rows, hidden] outputs of `dtype`.
+ *   z             : [rows, hidden] output of `dtype` or NULL (pre-norm keeps
+ *                   it as the next residual; post-norm passes NULL).
+ *   mean, rstd    : [rows] float32 or NULL; mean is written for LayerNorm only.
+ *   mask          : uint8 keep flags or NULL: [rows, hidden] for x0, followed
+ *                   by [rows, hidden] for x1 when x1 is given.
+ *   hidden        : a multiple of 8, at most 8192 (FA_ERR_SHAPE otherwise).
+ *   dropout_p     : 0 <= p < 1; eps > 0 and finite; norm an fa_norm value
+ *                   (FA_ERR_ARG otherwise).
+ *   dtype         : FA_F16 or FA_BF16 (FA_ERR_DTYPE otherwise).
+ * Arithmetic in fp32: z is formed and kept in fp32, then rounded to dtype
+ * for the z output only; mean and variance are two passes over z. Tensor
+ * pointers 16-byte aligned, mean / rstd 4-byte aligned (FA_ERR_ALIGN);
+ * outputs must not overlap inputs or each other (FA_ERR_ALIAS). rows = 0
+ * or hidden = 0 is a no-op. Returns an fa_status.
+ */
+int fa_dropout_add_norm(const void* x0, const void* x1, const void* residual,
+                        const void* gamma0, const void* beta0, const void* gamma1,
+                        const void* beta1, void* y0, void* y1, void* z, float* mean,
+                        float* rstd, unsigned char* mask, int rows, int hidden,
+                        float dropout_p, uint64_t seed, uint64_t offset, float eps,
+                        int norm, int dtype, void* stream);
 
 /*
  * Dense backward: the gradients of sum(O * dO) with respect to Q, K and V.

@@ -85,10 +85,13 @@ def keep_threshold(p) -> int:
     return int(np.floor(p32 * 4294967296.0))
 
 
-def dropout_keep(rows: int, hidden: int, p, seed: int, offset: int, stream: int = 0):
-    """Boolean keep mask [rows, hidden] of one branch."""
+def dropout_keep(rows: int, hidden: int, p, seed: int, offset: int, stream: int = 0,
+                 row_ids=None):
+    """Boolean keep mask [rows, hidden] of one branch; row_ids gives the global
+    row index of each of the rows (default 0 .. rows-1)."""
     thr = keep_threshold(p)
-    e = np.arange(rows * hidden, dtype=np.uint64)
+    ids = np.arange(rows, dtype=np.uint64) if row_ids is None else np.asarray(row_ids, np.uint64)
+    e = (ids[:, None] * np.uint64(hidden) + np.arange(hidden, dtype=np.uint64)[None, :]).reshape(-1)
     q = e // np.uint64(4)
     ctr = np.empty(q.shape + (4,), dtype=np.uint64)
     ctr[:, 0] = q & _M32
@@ -102,17 +105,18 @@ def dropout_keep(rows: int, hidden: int, p, seed: int, offset: int, stream: int 
 
 def dropout_add_norm(x0, gamma0, beta0=None, residual=None, x1=None, gamma1=None, beta1=None,
                      p: float = 0.0, seed: int = 0, offset: int = 0, eps: float = 1e-5,
-                     rms: bool = False):
+                     rms: bool = False, row_ids=None):
     """x0, x1, residual: [rows, hidden]; gamma/beta: [hidden]. Returns a dict
-    with y0, y1 (or None), z, mean (None for RMSNorm), rstd, keep0, keep1."""
+    with y0, y1 (or None), z, mean (None for RMSNorm), rstd, keep0, keep1.
+    row_ids: global row indices of the given rows (for the dropout counters)."""
     x0 = _f64(x0)
     rows, hidden = x0.shape
     keep_scale = 1.0 / (1.0 - float(np.float32(p)))
-    keep0 = dropout_keep(rows, hidden, p, seed, offset, 0)
+    keep0 = dropout_keep(rows, hidden, p, seed, offset, 0, row_ids)
     z = np.where(keep0, x0 * keep_scale, 0.0)                        # dropout(x0)
     keep1 = None
     if x1 is not None:
-        keep1 = dropout_keep(rows, hidden, p, seed, offset, 1)
+        keep1 = dropout_keep(rows, hidden, p, seed, offset, 1, row_ids)
         z = z + np.where(keep1, _f64(x1) * keep_scale, 0.0)          # + dropout(x1)
     if residual is not None:
         z = z + _f64(residual)                                       # + residual

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert fa.fa_version() == 400
+    assert fa.fa_version() == 500
     for code, name in fa.STATUS.items():
         assert fa.fa_strerror(code).startswith(name)
     assert fa.fa_strerror(12345) == "unknown fa_status"
@@ -196,3 +196,44 @@ def test_kv_outer_validation(lib, kw, status):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=0, groups=0 + 1)])
 def test_kv_outer_empty_is_noop(lib, kw):
     assert kv_outer(lib, **kw) == 0
+
+
+# fa_dropout_add_norm: thirteen buffers at distinct fake addresses.
+NM = {name: 0x10000000 * (i + 1) for i, name in enumerate(
+    ("x0", "x1", "res", "g0", "b0", "g1", "b1", "y0", "y1", "z", "mean", "rstd", "mask"))}
+
+
+def norm(lib, rows=64, hidden=1024, p=0.1, seed=1, offset=0, eps=1e-5, kind=0,
+         dtype=fa.FA_BF16, **ptrs):
+    a = dict(NM, **ptrs)
+    return lib.fa_dropout_add_norm(a["x0"], a["x1"], a["res"], a["g0"], a["b0"], a["g1"],
+                                   a["b1"], a["y0"], a["y1"], a["z"], a["mean"], a["rstd"],
+                                   a["mask"], rows, hidden, p, seed, offset, eps, kind, dtype,
+                                   None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=fa.FA_F32), -4), (dict(dtype=4), -4),
+    (dict(rows=-1), -2), (dict(hidden=-8), -2), (dict(hidden=1020), -2), (dict(hidden=8200), -2),
+    (dict(kind=2), -10), (dict(p=1.0), -10), (dict(p=-0.1), -10), (dict(p=float("nan")), -10),
+    (dict(eps=0.0), -10), (dict(eps=float("inf")), -10),
+    (dict(x0=0), -1), (dict(g0=0), -1), (dict(y0=0), -1), (dict(y1=0), -1), (dict(g1=0), -1),
+    (dict(g1=0, y1=0, b1=NM["b1"]), -1),
+    (dict(x1=NM["x1"] + 8), -5), (dict(mask=NM["mask"] + 4), -5), (dict(rstd=NM["rstd"] + 2), -5),
+    (dict(y0=NM["x0"]), -6), (dict(z=NM["res"] + 32), -6), (dict(mean=NM["g0"]), -6),
+    (dict(rstd=NM["y1"] + 64), -6), (dict(mask=NM["z"]), -6),
+])
+def test_norm_validation(lib, kw, status):
+    assert norm(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(rows=0), dict(hidden=0), dict(rows=0, x0=0)])
+def test_norm_empty_is_noop(lib, kw):
+    assert norm(lib, **kw) == 0
+
+
+def test_norm_optional_pointers_accepted_as_null(lib):
+    # post-norm, no residual, no second branch or output, no stats: validation
+    # passes, then an empty problem launches nothing
+    assert norm(lib, rows=0, x1=0, res=0, b0=0, g1=0, b1=0, y1=0, z=0, mean=0, rstd=0,
+                mask=0) == 0

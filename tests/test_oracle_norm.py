@@ -158,3 +158,9 @@ def test_parallel_residual_and_second_output():
     zn = (z - z.mean(1, keepdims=True)) / np.sqrt(z.var(1, keepdims=True) + 1e-5)
     np.testing.assert_allclose(out["y1"], zn * g1 + b1, atol=1e-12)
     assert (out["keep0"] != out["keep1"]).mean() > 0.2
+
+
+def test_row_ids_select_rows_of_the_full_mask():
+    full = oracle.dropout_keep(50, 24, 0.4, seed=8, offset=3, stream=1)
+    sub = oracle.dropout_keep(3, 24, 0.4, seed=8, offset=3, stream=1, row_ids=[0, 17, 49])
+    np.testing.assert_array_equal(sub, full[[0, 17, 49]])

@@ -204,3 +204,44 @@ def traffic_kv_outer(n: int, d: int, Bc: int, elem: int, groups: int = 1, acc: i
 def traffic_total(t: dict) -> tuple:
     """(bytes read, bytes written) of a traffic dict."""
     return sum(r for r, _ in t.values()), sum(w for _, w in t.values())
+
+
+# Fused dropout + residual + norm workloads: the rows are the tokens of the
+# attention workload above (B*N = 2*8192) and the hidden size its H*d = 4096
+# (the attention output entering the residual stream), plus the largest hidden
+# size the op supports with a parallel second branch and RMSNorm.
+NORM_WORKLOADS = {
+    "post_attention_ln_bf16": dict(rows=16384, hidden=4096, dtype="bf16", p=0.1, rms=False,
+                                   x1=False, residual=True, gamma1=False, prenorm=True, seed=21),
+    "parallel_rms_8192_bf16": dict(rows=8192, hidden=8192, dtype="bf16", p=0.1, rms=True,
+                                   x1=True, residual=True, gamma1=True, prenorm=True, seed=22),
+}
+
+
+def norm_inputs(rows: int, hidden: int, dtype: str, seed: int = 0, x1: bool = False,
+                residual: bool = True, beta: bool = True, gamma1: bool = False):
+    """x0, x1, residual ~ N(0,1) [rows, hidden]; gamma ~ 1 + 0.1 N(0,1),
+    beta ~ 0.1 N(0,1) [hidden]; drawn in that order as float32 and rounded to
+    dtype. Absent tensors are None (and draw nothing)."""
+    rng = np.random.default_rng(seed)
+    t = DTYPES[dtype]
+    draw = lambda shape, mul=1.0, add=0.0: torch.from_numpy(
+        (add + mul * rng.standard_normal(shape, dtype=np.float32)).astype(np.float32)).to(t)
+    out = {"x0": draw((rows, hidden))}
+    out["x1"] = draw((rows, hidden)) if x1 else None
+    out["residual"] = draw((rows, hidden)) if residual else None
+    out["gamma0"] = draw((hidden,), 0.1, 1.0)
+    out["beta0"] = draw((hidden,), 0.1) if beta else None
+    out["gamma1"] = draw((hidden,), 0.1, 1.0) if gamma1 else None
+    out["beta1"] = draw((hidden,), 0.1) if gamma1 and beta else None
+    return out
+
+
+def norm_bytes(rows: int, hidden: int, elem: int, x1: bool, residual: bool, gamma1: bool,
+               prenorm: bool, stats: int = 2) -> int:
+    """Compulsory HBM bytes of one fused dropout + residual + norm call: each
+    row input read once, each output written once, weights once, stats."""
+    row_in = 1 + int(x1) + int(residual)
+    row_out = 1 + int(gamma1) + int(prenorm)
+    weights = 2 * (1 + int(gamma1))
+    return (row_in + row_out) * rows * hidden * elem + weights * hidden * elem + stats * rows * 4
