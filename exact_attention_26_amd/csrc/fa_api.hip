@@ -44,13 +44,13 @@ int check_buffers(const void* Q, const void* K, const void* V, const void* O, co
   return FA_OK;
 }
 
-int launch(const fa::FwdParams& p, int d, int dtype, bool varlen, void* stream) {
+int launch(const fa::FwdParams& p, int d, int dtype, bool varlen, void* stream, int waves = 8) {
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == FA_F32)
     e = fa::launch_fwd_f32(p, d, varlen, s);
   else
-    e = fa::launch_fwd_mfma16(p, d, dtype == FA_BF16, varlen, s);
+    e = fa::launch_fwd_mfma16(p, d, dtype == FA_BF16, varlen, waves, s);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -106,7 +106,11 @@ int fa_fwd_banded(const void* Q, const void* K, const void* V, void* O, float* L
   if (B == 0 || H == 0 || N == 0) return FA_OK;
 
   if ((int64_t)N * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
-  const int br = fa::kRowsPerBlock16;
+  // Narrow bands visit few key tiles per block: 4-wave, 128-row workgroups
+  // (two per CU) overlap one another's loads with compute.
+  const int wcap = window < N ? window : N;  // a window of N or more keeps every key
+  const int waves = wcap <= fa::kBandNarrowMax ? fa::kBandNarrowWaves : fa::kWaves16;
+  const int br = 32 * waves;
   if ((int64_t)((N + br - 1) / br) * H * B > kMaxBlocks) return FA_ERR_SIZE;
   const uint64_t elems = (uint64_t)B * H * N * d;
   const int st = check_buffers(Q, K, V, O, L, elems * 2, (uint64_t)B * H * N * 4);
@@ -129,8 +133,8 @@ int fa_fwd_banded(const void* Q, const void* K, const void* V, void* O, float* L
   p.q_blocks = (N + br - 1) / br;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
-  p.window = window < N ? window : N;  // a window of N or more keeps every key
-  return launch(p, d, dtype, false, stream);
+  p.window = wcap;
+  return launch(p, d, dtype, false, stream, waves);
 }
 
 int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L,

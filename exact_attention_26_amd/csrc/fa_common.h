@@ -110,7 +110,9 @@ struct NormParams {
 
 // Launchers; return 0 on success or a hipError_t from the launch.
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool varlen, hipStream_t stream);
-hipError_t launch_fwd_mfma16(const FwdParams& p, int d, bool bf16, bool varlen,
+// waves: 8 (ping-pong, 256-row workgroups) or 4 (banded only, 128-row workgroups);
+// p.q_blocks must count blocks of 32 * waves rows.
+hipError_t launch_fwd_mfma16(const FwdParams& p, int d, bool bf16, bool varlen, int waves,
                              hipStream_t stream);
 hipError_t launch_dropout_add_norm(const NormParams& p, bool bf16, hipStream_t stream);
 hipError_t launch_fwd_kv_outer(const KvOuterParams& p, int d, bool bf16, hipStream_t stream);
@@ -121,12 +123,20 @@ constexpr int kBwdKeysPerBlock = 128;
 constexpr int kBwdQueriesPerBlock = 128;
 
 // Rows of Q owned by one workgroup of each kernel (sizes the grid). The
-// 16-bit kernel runs kWaves16 waves of 32 query rows each.
+// 16-bit kernel runs kWaves16 waves of 32 query rows each (the banded entry
+// may run 4 instead: kBandNarrowWaves, below).
 #ifndef FA_WAVES16
 #define FA_WAVES16 8
 #endif
 constexpr int kWaves16 = FA_WAVES16;
 constexpr int kRowsPerBlockF32 = 128;
 constexpr int kRowsPerBlock16 = 32 * kWaves16;
+// Banded forward: windows up to this many keys run the 4-wave variant
+// (measured faster from w = 0, 1.56x, to w = 2048, 1.02x; slower from 4096).
+#ifndef FA_BAND_NARROW_MAX
+#define FA_BAND_NARROW_MAX 2048
+#endif
+constexpr int kBandNarrowMax = FA_BAND_NARROW_MAX;
+constexpr int kBandNarrowWaves = 4;
 
 }  // namespace fa

@@ -68,9 +68,6 @@
 namespace fa {
 namespace {
 
-constexpr int kWaves = kWaves16;
-constexpr int kThreads = 64 * kWaves;
-constexpr int BR = kRowsPerBlock16;  // query rows per workgroup (32 per wave)
 constexpr int BC = 64;               // keys per tile
 // Waves that issue the K/V copies (group B, waves 4-7).
 constexpr int kDmaWaves = 4;
@@ -95,8 +92,17 @@ struct Tile {
 // workgroup visits only the key tiles that hold a key within the window of
 // one of its rows, and masks per element only in the tiles where the band
 // edge cuts a wave's 32 x 64 block.
-template <bool BF16, int D, bool VARLEN, bool BAND>
-__global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
+//
+// NW: waves per workgroup. 8 (the default) runs the ping-pong of two wave
+// groups described below, one workgroup per CU. 4 runs a single group (every
+// wave issues its share of the copies and takes both barriers of a step) in
+// 128-row workgroups, two per CU: their load, compute and store phases then
+// overlap each other, which pays off when a workgroup visits only a few key
+// tiles (narrow bands).
+template <bool BF16, int D, bool VARLEN, bool BAND, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
+  static_assert(NW == 8 || NW == 4, "8 waves (ping-pong) or 4 (one group)");
+  constexpr int BR = 32 * NW;  // query rows per workgroup (32 per wave)
   using vec8 = typename Elem<BF16>::vec8;
   using T = Tile<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * T::STAGEB];
@@ -279,7 +285,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
     return BAND && (kb + BC - 1 - row0 > win || row0 + 31 - kb > win);
   };
 
-  static_assert(kWaves == 8, "ping-pong pairs waves w and w+4 on one SIMD");
   // Ping-pong: waves 0-3 (group A) and 4-7 (group B) share the four SIMDs,
   // one of each per SIMD, and run half a step apart. Between two workgroup
   // barriers one wave of every SIMD is in its matrix half (MFMAs only: S^T
@@ -288,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
   // dtype); at the next barrier they swap. The matrix core and the VALU of
   // a SIMD thus work for different waves at the same time, which overlaps
   // far better than MFMAs and exponentials issued by one wave.
-  const bool grp_a = wave < 4;
+  const bool grp_a = NW == 8 && wave < 4;  // with NW = 4 every wave is in group B
   vec8 pb[4];           // P of the current tile, storage dtype: P.V B operands
   // Running max of raw q.k (scale > 0). With a band it starts at a large
   // finite negative value instead of -inf: a row may meet whole tiles with
@@ -482,24 +487,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd16_kernel(FwdParams p) {
 }
 
 template <bool BF16, int D>
-const void* pick(bool varlen, bool band) {
-  if (band) return (const void*)fwd16_kernel<BF16, D, false, true>;
-  return varlen ? (const void*)fwd16_kernel<BF16, D, true, false>
-                : (const void*)fwd16_kernel<BF16, D, false, false>;
+const void* pick(bool varlen, bool band, int waves) {
+  if (band)
+    return waves == 4 ? (const void*)fwd16_kernel<BF16, D, false, true, 4>
+                      : (const void*)fwd16_kernel<BF16, D, false, true, 8>;
+  return varlen ? (const void*)fwd16_kernel<BF16, D, true, false, 8>
+                : (const void*)fwd16_kernel<BF16, D, false, false, 8>;
 }
 
 }  // namespace
 
-hipError_t launch_fwd_mfma16(const FwdParams& p, int d, bool bf16, bool varlen,
+hipError_t launch_fwd_mfma16(const FwdParams& p, int d, bool bf16, bool varlen, int waves,
                              hipStream_t stream) {
   const bool band = p.window >= 0;
   const void* fn = nullptr;
   if (bf16)
-    fn = (d == 64) ? pick<true, 64>(varlen, band) : pick<true, 128>(varlen, band);
+    fn = (d == 64) ? pick<true, 64>(varlen, band, waves) : pick<true, 128>(varlen, band, waves);
   else
-    fn = (d == 64) ? pick<false, 64>(varlen, band) : pick<false, 128>(varlen, band);
+    fn = (d == 64) ? pick<false, 64>(varlen, band, waves) : pick<false, 128>(varlen, band, waves);
   const dim3 grid((unsigned)((int64_t)p.q_blocks * p.H * p.B));
-  const dim3 block(kThreads);
+  const dim3 block(64 * waves);
   FwdParams arg = p;
   void* args[] = {&arg};
   return hipLaunchKernel(fn, grid, block, args, 0, stream);
