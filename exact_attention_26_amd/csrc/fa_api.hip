@@ -25,10 +25,6 @@ int elem_bytes(int dtype) { return dtype == FA_F32 ? 4 : 2; }
 
 bool valid_dtype(int dtype) { return dtype == FA_F32 || dtype == FA_F16 || dtype == FA_BF16; }
 
-int rows_per_block(int dtype) {
-  return dtype == FA_F32 ? fa::kRowsPerBlockF32 : fa::kRowsPerBlock16;
-}
-
 // Shared checks on the dense and varlen entry points after the sizes are
 // known to be non-negative and non-empty.
 int check_buffers(const void* Q, const void* K, const void* V, const void* O, const float* L,
@@ -70,7 +66,8 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B
   if (B == 0 || H == 0 || N == 0) return FA_OK;
 
   if ((int64_t)N * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
-  const int br = rows_per_block(dtype);
+  const int waves = (dtype != FA_F32 && N <= fa::kDenseNarrowMaxN) ? 4 : 8;
+  const int br = dtype == FA_F32 ? fa::kRowsPerBlockF32 : 32 * waves;
   if ((int64_t)((N + br - 1) / br) * H * B > kMaxBlocks) return FA_ERR_SIZE;
   const uint64_t elems = (uint64_t)B * H * N * d;
   const int st = check_buffers(Q, K, V, O, L, elems * elem_bytes(dtype), (uint64_t)B * H * N * 4);
@@ -94,7 +91,7 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.window = -1;
-  return launch(p, d, dtype, false, stream);
+  return launch(p, d, dtype, false, stream, waves);
 }
 
 int fa_fwd_banded(const void* Q, const void* K, const void* V, void* O, float* L, int B, int H,
@@ -148,7 +145,8 @@ int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L
   if (nseq == 0 || total_tokens == 0 || max_seqlen == 0 || H == 0) return FA_OK;
 
   if ((int64_t)max_seqlen * H * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
-  const int br = rows_per_block(dtype);
+  const int waves = (dtype != FA_F32 && max_seqlen <= fa::kVarlenNarrowMaxN) ? 4 : 8;
+  const int br = dtype == FA_F32 ? fa::kRowsPerBlockF32 : 32 * waves;
   if ((int64_t)((max_seqlen + br - 1) / br) * H * nseq > kMaxBlocks) return FA_ERR_SIZE;
   if (!cu_seqlens) return FA_ERR_NULL;
   const uint64_t elems = (uint64_t)total_tokens * H * d;
@@ -179,7 +177,7 @@ int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.window = -1;
-  return launch(p, d, dtype, true, stream);
+  return launch(p, d, dtype, true, stream, waves);
 }
 
 int fa_fwd_kv_outer(const void* Q, const void* K, const void* V, void* O, float* L, float* acc,

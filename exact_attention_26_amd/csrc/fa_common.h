@@ -123,8 +123,8 @@ constexpr int kBwdKeysPerBlock = 128;
 constexpr int kBwdQueriesPerBlock = 128;
 
 // Rows of Q owned by one workgroup of each kernel (sizes the grid). The
-// 16-bit kernel runs kWaves16 waves of 32 query rows each (the banded entry
-// may run 4 instead: kBandNarrowWaves, below).
+// 16-bit kernel runs kWaves16 waves of 32 query rows each, or 4 waves (128
+// rows) for short sequences and narrow bands (thresholds below).
 #ifndef FA_WAVES16
 #define FA_WAVES16 8
 #endif
@@ -138,5 +138,17 @@ constexpr int kRowsPerBlock16 = 32 * kWaves16;
 #endif
 constexpr int kBandNarrowMax = FA_BAND_NARROW_MAX;
 constexpr int kBandNarrowWaves = 4;
+// Dense and packed forward: sequences up to these lengths run the 4-wave
+// variant too (measured back to back: dense d = 64, N = 512 +12 %, N = 2048
+// +10 %; d = 128, N = 1024 +5 %, N = 4096 -2 %, N = 8192 -3 %; varlen with
+// lengths 64..4096 +4 %, 64..1024 +29 %). Outputs are bitwise identical.
+#ifndef FA_DENSE_NARROW_MAX_N
+#define FA_DENSE_NARROW_MAX_N 2048
+#endif
+#ifndef FA_VARLEN_NARROW_MAX_N
+#define FA_VARLEN_NARROW_MAX_N 4096
+#endif
+constexpr int kDenseNarrowMaxN = FA_DENSE_NARROW_MAX_N;
+constexpr int kVarlenNarrowMaxN = FA_VARLEN_NARROW_MAX_N;
 
 }  // namespace fa

@@ -98,7 +98,7 @@ struct Tile {
 // wave issues its share of the copies and takes both barriers of a step) in
 // 128-row workgroups, two per CU: their load, compute and store phases then
 // overlap each other, which pays off when a workgroup visits only a few key
-// tiles (narrow bands).
+// tiles (narrow bands, short sequences).
 template <bool BF16, int D, bool VARLEN, bool BAND, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   static_assert(NW == 8 || NW == 4, "8 waves (ping-pong) or 4 (one group)");
@@ -491,8 +491,11 @@ const void* pick(bool varlen, bool band, int waves) {
   if (band)
     return waves == 4 ? (const void*)fwd16_kernel<BF16, D, false, true, 4>
                       : (const void*)fwd16_kernel<BF16, D, false, true, 8>;
-  return varlen ? (const void*)fwd16_kernel<BF16, D, true, false, 8>
-                : (const void*)fwd16_kernel<BF16, D, false, false, 8>;
+  if (varlen)
+    return waves == 4 ? (const void*)fwd16_kernel<BF16, D, true, false, 4>
+                      : (const void*)fwd16_kernel<BF16, D, true, false, 8>;
+  return waves == 4 ? (const void*)fwd16_kernel<BF16, D, false, false, 4>
+                    : (const void*)fwd16_kernel<BF16, D, false, false, 8>;
 }
 
 }  // namespace
