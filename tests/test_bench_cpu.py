@@ -1,0 +1,78 @@
+"""bench.py's host-side logic, without a GPU: the multi-GPU refusal, the
+counter-summary reader and its source-hash check, the clock-sampler helper
+protocol, and the byte accounting of the fused norm workloads."""
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import workloads  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused(monkeypatch, capsys):
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--gpus", "2"])
+    assert bench.main() == 2
+    assert "one GPU only" in capsys.readouterr().err
+
+
+def test_pmc_reader_checks_the_source_hash(tmp_path, monkeypatch):
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    # the hash is computed from the real kernel sources
+    monkeypatch.setattr(bench, "kernel_source_hash",
+                        lambda order="q_outer": {"q_outer": "aaaa", "norm": "bbbb"}[order])
+    (prof / "fa_fwd_w_pmc.txt").write_text(
+        "# header: not parsed\nkernel_source_sha: aaaa\nhbm_bytes_per_launch: 12345\n")
+    assert bench.read_pmc_traffic("w") == 12345
+    (prof / "fa_norm_w_pmc.txt").write_text("kernel_source_sha: old\nhbm_bytes_per_launch: 7\n")
+    assert bench.read_pmc_traffic("w", order="norm") is None      # stale summary
+    assert bench.read_pmc_traffic("missing") is None
+
+
+def test_source_hash_is_per_kernel():
+    hashes = {k: bench.kernel_source_hash(k) for k in bench.KERNEL_SOURCES}
+    assert len(set(hashes[k] for k in ("q_outer", "kv_outer", "norm"))) == 3
+    assert hashes["band"] == hashes["q_outer"]  # the banded forward is the same source file
+
+
+def test_clock_sampler_protocol(tmp_path, monkeypatch):
+    fake = tmp_path / "amd-smi"
+    fake.write_text("#!/bin/sh\necho 'GPU: 0'\necho '    GFX_0:'\necho '        CLK: 2100 MHz'\n"
+                    "echo '    GFX_1:'\necho '        CLK: 1900 MHz'\necho '    MEM_0:'\n"
+                    "echo '        CLK: 1300 MHz'\necho '    SOCKET_POWER: 1300 W'\n")
+    fake.chmod(0o755)
+    monkeypatch.setenv("PATH", f"{tmp_path}:{os.environ['PATH']}")
+    import torch
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: None)
+    bench.start_sclk_sampler()
+    try:
+        mhz, watts = bench.sample_sclk(lambda: None, seconds=0.2)
+    finally:
+        bench._sampler.stdin.close()
+        bench._sampler.wait(timeout=10)
+        bench._sampler = None
+    assert mhz == pytest.approx(2000.0) and watts == pytest.approx(1300.0)  # MEM clock excluded
+
+
+def test_sampler_absent_gives_nulls(monkeypatch):
+    monkeypatch.setattr(bench, "_sampler", None)
+    assert bench.sample_sclk(lambda: None, seconds=0.0) == (None, None)
+
+
+@pytest.mark.parametrize("name", sorted(workloads.NORM_WORKLOADS))
+def test_norm_bytes_count_every_tensor_once(name):
+    w = workloads.NORM_WORKLOADS[name]
+    rows, hidden = w["rows"], w["hidden"]
+    inputs = 1 + w["x1"] + w["residual"]
+    outputs = 1 + w["gamma1"] + w["prenorm"]
+    weights = 2 * (1 + w["gamma1"])
+    stats = 1 if w["rms"] else 2
+    want = (inputs + outputs) * rows * hidden * 2 + weights * hidden * 2 + stats * rows * 4
+    got = workloads.norm_bytes(rows, hidden, 2, w["x1"], w["residual"], w["gamma1"],
+                               w["prenorm"], stats=stats)
+    assert got == want
