@@ -11,6 +11,29 @@
 
 namespace {
 
+// Wave count of the 16-bit forward's workgroups: 8 runs the ping-pong of two
+// wave groups (256 rows), 4 a single group (128 rows, two workgroups per CU),
+// which wins whenever a workgroup visits few key tiles. Measured back to back,
+// with bitwise-identical outputs:
+// - banded: faster from w = 0 (1.56x) to w = 2048 (1.02x), slower from 4096;
+// - dense: d = 64, N = 512 +12 %, N = 2048 +10 %; d = 128, N = 1024 +5 %,
+//   N = 4096 -2 %, N = 8192 -3 %;
+// - varlen: lengths 64..4096 +4 %, 64..1024 +29 %.
+#ifndef FA_BAND_NARROW_MAX
+#define FA_BAND_NARROW_MAX 2048
+#endif
+#ifndef FA_DENSE_NARROW_MAX_N
+#define FA_DENSE_NARROW_MAX_N 2048
+#endif
+#ifndef FA_VARLEN_NARROW_MAX_N
+#define FA_VARLEN_NARROW_MAX_N 4096
+#endif
+constexpr int kWavesPingPong = 8;
+constexpr int kWavesNarrow = 4;
+constexpr int kBandNarrowMax = FA_BAND_NARROW_MAX;     // windows (capped at N)
+constexpr int kDenseNarrowMaxN = FA_DENSE_NARROW_MAX_N;
+constexpr int kVarlenNarrowMaxN = FA_VARLEN_NARROW_MAX_N;  // max_seqlen
+
 constexpr int kVersion = 500;  // 0.5.0: adds fa_dropout_add_norm
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -40,7 +63,8 @@ int check_buffers(const void* Q, const void* K, const void* V, const void* O, co
   return FA_OK;
 }
 
-int launch(const fa::FwdParams& p, int d, int dtype, bool varlen, void* stream, int waves = 8) {
+int launch(const fa::FwdParams& p, int d, int dtype, bool varlen, void* stream,
+           int waves = kWavesPingPong) {
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e;
   if (dtype == FA_F32)
@@ -66,7 +90,7 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B
   if (B == 0 || H == 0 || N == 0) return FA_OK;
 
   if ((int64_t)N * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
-  const int waves = (dtype != FA_F32 && N <= fa::kDenseNarrowMaxN) ? 4 : 8;
+  const int waves = (dtype != FA_F32 && N <= kDenseNarrowMaxN) ? kWavesNarrow : kWavesPingPong;
   const int br = dtype == FA_F32 ? fa::kRowsPerBlockF32 : 32 * waves;
   if ((int64_t)((N + br - 1) / br) * H * B > kMaxBlocks) return FA_ERR_SIZE;
   const uint64_t elems = (uint64_t)B * H * N * d;
@@ -106,7 +130,7 @@ int fa_fwd_banded(const void* Q, const void* K, const void* V, void* O, float* L
   // Narrow bands visit few key tiles per block: 4-wave, 128-row workgroups
   // (two per CU) overlap one another's loads with compute.
   const int wcap = window < N ? window : N;  // a window of N or more keeps every key
-  const int waves = wcap <= fa::kBandNarrowMax ? fa::kBandNarrowWaves : fa::kWaves16;
+  const int waves = wcap <= kBandNarrowMax ? kWavesNarrow : kWavesPingPong;
   const int br = 32 * waves;
   if ((int64_t)((N + br - 1) / br) * H * B > kMaxBlocks) return FA_ERR_SIZE;
   const uint64_t elems = (uint64_t)B * H * N * d;
@@ -145,7 +169,7 @@ int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L
   if (nseq == 0 || total_tokens == 0 || max_seqlen == 0 || H == 0) return FA_OK;
 
   if ((int64_t)max_seqlen * H * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
-  const int waves = (dtype != FA_F32 && max_seqlen <= fa::kVarlenNarrowMaxN) ? 4 : 8;
+  const int waves = (dtype != FA_F32 && max_seqlen <= kVarlenNarrowMaxN) ? kWavesNarrow : kWavesPingPong;
   const int br = dtype == FA_F32 ? fa::kRowsPerBlockF32 : 32 * waves;
   if ((int64_t)((max_seqlen + br - 1) / br) * H * nseq > kMaxBlocks) return FA_ERR_SIZE;
   if (!cu_seqlens) return FA_ERR_NULL;

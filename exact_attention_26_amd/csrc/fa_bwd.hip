@@ -38,6 +38,7 @@
 // consecutive rows a transposed read touches.
 #include <type_traits>
 
+#include "fa_bwd_params.h"
 #include "fa_device.h"
 
 namespace fa {

@@ -15,7 +15,7 @@
 //    from LDS in its natural row-major order.
 //  * K rows are padded by one float in LDS (conflict-free column reads),
 //    V rows by four floats; two LDS stages, one barrier per tile.
-#include "fa_device.h"
+#include "fa_fwd_unit.h"
 
 namespace fa {
 namespace {

@@ -23,6 +23,7 @@
 // v_mfma_f32_32x32x16, one query per lane. The softmax is the exact online
 // update (row max every tile).
 #include "fa_device.h"
+#include "fa_kvouter_params.h"
 
 namespace fa {
 namespace {

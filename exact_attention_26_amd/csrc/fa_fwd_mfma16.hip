@@ -44,7 +44,7 @@
 //    row max are skipped while the sums of p show that no p exceeds 2^8.
 #include <type_traits>
 
-#include "fa_device.h"
+#include "fa_fwd_unit.h"
 
 // Build options (defaults are the shipped configuration):
 //   FA_RESCALE_TAU (8): the reference max m of the running sums moves (and

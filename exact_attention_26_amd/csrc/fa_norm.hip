@@ -25,6 +25,7 @@
 // of the W partial sums through LDS. Mean and variance are two passes over
 // the registers (no cancellation from E[z^2] - E[z]^2).
 #include "fa_device.h"
+#include "fa_norm_params.h"
 
 // Build option FA_NORM_NT (1): row loads and stores are non-temporal (every
 // row element is touched once; measured 6-9 % faster than plain accesses).
