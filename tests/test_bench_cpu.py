@@ -76,3 +76,13 @@ def test_norm_bytes_count_every_tensor_once(name):
     got = workloads.norm_bytes(rows, hidden, 2, w["x1"], w["residual"], w["gamma1"],
                                w["prenorm"], stats=stats)
     assert got == want
+
+
+def test_seq_len_override_keeps_the_rest_of_the_workload():
+    base = workloads.make("short_bf16")
+    w = workloads.make("short_bf16", seq_len=96)
+    assert (w["B"], w["H"], w["N"], w["d"]) == (base["B"], base["H"], 96, base["d"])
+    assert w["q"].shape == (base["B"], base["H"], 96, base["d"]) and w["q"].dtype == base["q"].dtype
+    assert w["scale"] == base["scale"]
+    with pytest.raises(ValueError):
+        workloads.make("varlen_bf16", seq_len=96)

@@ -134,13 +134,18 @@ def varlen_inputs(lengths, H: int, d: int, dtype: str, seed: int = 0,
     return q, k, v, cu
 
 
-def make(name: str):
+def make(name: str, seq_len: int | None = None):
     """Inputs of a named workload.
 
-    Dense: returns dict(q,k,v, B,H,N,d, scale, dtype).
+    Dense: returns dict(q,k,v, B,H,N,d, scale, dtype); seq_len, if given,
+    replaces N (same B, H, d, dtype, distributions and seed).
     Varlen: returns dict(q,k,v, cu_seqlens, lengths, max_seqlen, H,d, scale, dtype).
     """
     w = WORKLOADS[name]
+    if seq_len is not None:
+        if w.varlen:
+            raise ValueError("seq_len applies to dense workloads only")
+        w = dataclasses.replace(w, N=int(seq_len))
     if w.varlen:
         rng = np.random.default_rng(w.seed)
         lengths = rng.integers(w.min_len, w.max_len, endpoint=True, size=w.nseq).astype(np.int64)
