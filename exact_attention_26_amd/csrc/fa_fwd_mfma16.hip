@@ -38,7 +38,10 @@
 //         lane l receives element l%4 of the 4-element vectors loaded by
 //         lanes l/4, l/4+4, l/4+8 and l/4+12.
 //    Both read patterns are free of LDS bank conflicts.
-//  * Two LDS stages each for K and V, K one tile ahead of V.
+//  * K runs one tile ahead of V. The 8-wave kernel keeps three LDS stages
+//    each of K and V (two for 4 waves), so that every wave can read the
+//    first operands of its next matrix half during its softmax half and
+//    start its MFMAs right after the barrier.
 //  * O (fp32) lives in MFMA accumulators for the whole loop, one query per
 //    lane, so the rescale by alpha is a per-lane scalar multiply. It and the
 //    row max are skipped while the sums of p show that no p exceeds 2^8.
@@ -103,9 +106,12 @@ template <bool BF16, int D, bool VARLEN, bool BAND, int NW>
 __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   static_assert(NW == 8 || NW == 4, "8 waves (ping-pong) or 4 (one group)");
   constexpr int BR = 32 * NW;  // query rows per workgroup (32 per wave)
+  // LDS stages for K (and for V). The ping-pong needs three so that the
+  // first group can read its next operands before the barrier (below).
+  constexpr int S = NW == 8 ? 3 : 2;
   using vec8 = typename Elem<BF16>::vec8;
   using T = Tile<D>;
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * T::STAGEB];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[S * T::STAGEB];
 
   WorkUnit u;
   if (!resolve_unit<VARLEN>(p, BR, u)) return;
@@ -133,10 +139,9 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
     qf[s] = __builtin_bit_cast(vec8, w);
   }
 
-  // LDS holds two K stages followed by two V stages. K runs one tile ahead
-  // of V: while tile j's P.V reads V stage j%2, the S^T of tile j+1 reads K
-  // stage (j+1)%2, and the copies in flight fill K stage j%2 (tile j+2) and
-  // V stage (j+1)%2 (tile j+1).
+  // LDS holds S K stages followed by S V stages; tile j of either lives in
+  // stage j % S. K runs one tile ahead of V: the matrix half of step j reads
+  // K of tile j+1 (for S^T) and V of tile j (for P.V).
   //
   // Direct-to-LDS copies: copy r of this wave fills bytes
   // [1024*(wave*NDMA + r), +1024) of a tile; lane i writes 16 bytes at
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   };
   auto fetch_v = [&](int stage, int kb, bool tail) {
     const unsigned short* Gt = Vg + (int64_t)kb * rs;
-    const unsigned dst = lds0 + (2 + stage) * T::TILEB;
+    const unsigned dst = lds0 + (S + stage) * T::TILEB;
     if (!tail) {
 #pragma unroll
       for (int r = 0; r < NDMA; ++r) dma(Gt, dst + r * 1024, FA_VOFF(r));
@@ -211,6 +216,25 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   const int vj = lane & 15, vb = lane >> 4;
   const int vrow = 4 * (vb >> 1) + (vj >> 2);
   const int vin = 32 * (vb & 1) + 8 * (vj & 3);  // byte offset inside the 64-byte chunk
+  // This lane's operand addresses in stage 0: K per 32-element chunk pair
+  // ss, V per 32-column block dt (the V swizzle of row 16t + 8h + vrow
+  // equals that of vrow, since 16t + 8h spans whole swizzle periods). Every
+  // other read adds a constant (stage, key block, row block) that fits the
+  // 16-bit offset of the LDS instructions; the empty asm keeps the compiler
+  // from re-deriving one base per stage.
+  static_assert((8 / T::ROWS_PER_256) % T::VCHUNKS == 0, "V swizzle period");
+  const lds_u8* kp[D / 16];
+  const lds_u8* vp[D / 32];
+#pragma unroll
+  for (int ss = 0; ss < D / 16; ++ss) {
+    kp[ss] = (const lds_u8*)lds + l32 * T::ROWB + (((2 * ss + g) ^ kx) << 4);
+    __asm__ volatile("" : "+v"(kp[ss]));
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    vp[dt] = (const lds_u8*)lds + S * T::TILEB + vrow * T::ROWB + ((dt ^ T::vswz(vrow)) << 6) + vin;
+    __asm__ volatile("" : "+v"(vp[dt]));
+  }
 
   f32x16 o[D / 32];  // O^T accumulators: d = 32*t + 8*(i/4) + 4g + i%4, query l32
 #pragma unroll
@@ -223,7 +247,6 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   // S^T of the K tile in stage `stage`: lane holds query l32, keys
   // kt*32 + 8*(i/4) + 4*g + (i%4) in register i of s[kt].
   auto qk = [&](int stage, f32x16 (&s)[2]) {
-    const lds_u8* Ks = (const lds_u8*)lds + stage * T::TILEB;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -233,7 +256,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const vec8 a = *(const __attribute__((address_space(3))) vec8*)(
-            Ks + (kt * 32 + l32) * T::ROWB + (((2 * ss + g) ^ kx) << 4));
+            kp[ss] + stage * T::TILEB + kt * 32 * T::ROWB);
         s[kt] = mfma32x32x16<BF16>(a, qf[ss], s[kt]);
       }
   };
@@ -355,39 +378,40 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
     }
     __asm__ volatile("" : "+v"(l));
   };
-  // Matrix half of step t (stage parity P = t % 2): S^T of tile t+1 into sc
-  // from K stage 1-P (when HN) and O^T += V^T P^T of tile t from V stage P,
-  // the two MFMA streams interleaved.
-  auto matrix = [&](auto has_next, auto parity) {
-    constexpr bool HN = decltype(has_next)::value;
-    constexpr int P = decltype(parity)::value;
-    const lds_u8* Ks = (const lds_u8*)lds + (1 - P) * T::TILEB;
-    const lds_u8* Vs = (const lds_u8*)lds + (2 + P) * T::TILEB;
-    // Operand reads run FA_PP_AHEAD steps ahead of their MFMAs in rotating
-    // registers; sched_barrier keeps the compiler from hoisting them all.
-    constexpr int NSTEP = D / 8, DT = D / 32, AH = FA_PP_AHEAD, NB = AH + 1;
-    vec8 ka[NB];
-    i16x4 va[NB][2];
-    auto read = [&](int i) {
-      if constexpr (HN) {
-        const int ss = i >> 1, kt = i & 1;
-        ka[i % NB] = *(const __attribute__((address_space(3))) vec8*)(
-            Ks + (kt * 32 + l32) * T::ROWB + (((2 * ss + g) ^ kx) << 4));
-      }
-      const int t = i / DT, dt = i % DT;
+  // Operand registers of the matrix half. Reads run FA_PP_AHEAD MFMA steps
+  // ahead of their MFMAs in rotating registers; the first FA_PP_AHEAD reads
+  // of a matrix half are issued early, in the wave's preceding softmax half,
+  // so that its first MFMAs can start as soon as the barrier releases.
+  constexpr int NSTEP = D / 8, DT = D / 32, AH = FA_PP_AHEAD, NB = AH + 1;
+  static_assert(AH >= 1 && AH < NSTEP, "read-ahead depth");
+  vec8 ka[NB];
+  i16x4 va[NB][2];
+  // Operands of MFMA step i of a matrix half: the K chunk for S^T of the
+  // next tile (K stage KS) and the transposed V rows for P.V (V stage VS).
+  auto read = [&](auto kstage, auto vstage, int i) __attribute__((always_inline)) {
+    constexpr int KS = decltype(kstage)::value, VS = decltype(vstage)::value;
+    const int ss = i >> 1, kt = i & 1;
+    ka[i % NB] = *(const __attribute__((address_space(3))) vec8*)(
+        kp[ss] + KS * T::TILEB + kt * 32 * T::ROWB);
+    const int t = i / DT, dt = i % DT;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int row = 16 * t + 8 * h + vrow;
-        va[i % NB][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4*)(Vs + row * T::ROWB + ((dt ^ T::vswz(row)) << 6) + vin));
-      }
-    };
+    for (int h = 0; h < 2; ++h)
+      va[i % NB][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(vp[dt] + VS * T::TILEB + (16 * t + 8 * h) * T::ROWB));
+  };
+  auto preread = [&](auto kstage, auto vstage) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < AH; ++i) read(kstage, vstage, i);
+  };
+  // Matrix half of step t: S^T of tile t+1 into sc from K stage KS (when
+  // HN) and O^T += V^T P^T of tile t from V stage VS, the two MFMA streams
+  // interleaved. The reads of steps 0 .. AH-1 were issued by preread.
+  auto matrix = [&](auto has_next, auto kstage, auto vstage) {
+    constexpr bool HN = decltype(has_next)::value;
     __builtin_amdgcn_s_setprio(FA_PP_PRIO);
 #pragma unroll
-    for (int i = 0; i < AH; ++i) read(i);
-#pragma unroll
     for (int i = 0; i < NSTEP; ++i) {
-      if (i + AH < NSTEP) read(i + AH);
+      if (i + AH < NSTEP) read(kstage, vstage, i + AH);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (HN) {
         const int ss = i >> 1, kt = i & 1;
@@ -401,35 +425,52 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
     }
     __builtin_amdgcn_s_setprio(0);
   };
-  // Copies for step t (stage parity P): K of tile t+2 into K stage P (it
-  // held K of tile t, last read in step t-1) and V of tile t+1 into V stage
-  // 1-P (it held V of tile t-1, last read in step t-1).
-  auto prefetch = [&](auto parity, int t) {
-    constexpr int P = decltype(parity)::value;
-    if (t + 2 < tiles) fetch_k(P, (t0 + t + 2) * BC, t + 2 == rag);
-    if (t + 1 < tiles) fetch_v(1 - P, (t0 + t + 1) * BC, t + 1 == rag);
+  // Copies issued in the softmax half of step t: K of tile t+1+S into K
+  // stage (t+1) % S and V of tile t+S into V stage t % S. Both stages were
+  // last read in the matrix halves of step t, which every wave has finished
+  // at the barrier before. The copies complete (vmcnt(0)) at the end of the
+  // issuing waves' next matrix half, before the barrier after which the
+  // earliest reader, a preread, may run.
+  auto copies = [&](auto kstage, auto vstage, int t) {
+    constexpr int KS = decltype(kstage)::value, VS = decltype(vstage)::value;
+    if (t + 1 + S < tiles) fetch_k(KS, (t0 + t + 1 + S) * BC, t + 1 + S == rag);
+    if (t + S < tiles) fetch_v(VS, (t0 + t + S) * BC, t + S == rag);
   };
-  // Step t: [matrix(t)] | [softmax of tile t+1] |. Group B runs every step
-  // one half-step (one barrier) after group A, so on each SIMD the matrix
-  // half of one wave meets the softmax half of the other. Group B issues
-  // the copies for step t+1 at the start of its softmax half of step t and
-  // waits for them at the end of its matrix half of step t+1; that is
-  // before the barrier after which group A starts step t+2, the first to
-  // read them.
-  auto step = [&](auto has_next, auto parity, int t) {
-    constexpr int P = decltype(parity)::value;
-    matrix(has_next, parity);
+  // Step t (F = t % S): [matrix(t)] | [softmax of tile t+1] |. With 8
+  // waves, group B runs every step one half-step (one barrier) after group
+  // A, so on each SIMD the matrix half of one wave meets the softmax half of
+  // the other. Group B issues the copies. At the start of its softmax half
+  // each wave reads the first operands of its next matrix half (K of tile
+  // t+2, V of tile t+1): with three stages those tiles completed a full step
+  // earlier, so group A may read them while group B's copies of the step
+  // before are still in flight into other stages.
+  auto step = [&](auto has_next, auto phase, int t) {
+    constexpr int F = decltype(phase)::value;
+    using KS = std::integral_constant<int, (F + 1) % S>;
+    using VS = std::integral_constant<int, F>;
+    using KN = std::integral_constant<int, (F + 2) % S>;
+    using VN = std::integral_constant<int, (F + 1) % S>;
+    matrix(has_next, KS{}, VS{});
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (!grp_a) prefetch(std::integral_constant<int, 1 - P>{}, t + 1);
-    if constexpr (decltype(has_next)::value) softmax(t + 1 == rag, (t0 + t + 1) * BC);
+    if constexpr (decltype(has_next)::value) {
+      preread(KN{}, VN{});
+      if (!grp_a) copies(KS{}, VS{}, t);
+      softmax(t + 1 == rag, (t0 + t + 1) * BC);
+    }
     __syncthreads();
   };
 
+  // Prologue: tiles 0 .. S-1 of K and 0 .. S-2 of V; S^T and softmax of tile
+  // 0; the first operands of matrix half 0 (K stage 1, V stage 0); then the
+  // copies that step -1 would have issued (K of tile S, V of tile S-1).
   if (!grp_a) {
-    fetch_k(0, t0 * BC, rag == 0);
-    fetch_v(0, t0 * BC, rag == 0);
-    if (tiles > 1) fetch_k(1, (t0 + 1) * BC, rag == 1);
+#pragma unroll
+    for (int i = 0; i < S; ++i)
+      if (i < tiles) fetch_k(i, (t0 + i) * BC, rag == i);
+#pragma unroll
+    for (int i = 0; i + 1 < S; ++i)
+      if (i < tiles) fetch_v(i, (t0 + i) * BC, rag == i);
   }
   // Consume Q here, after the first copies are issued, so its load latency
   // overlaps theirs and the compiler waits for these loads before the key
@@ -440,27 +481,52 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   qk(0, sc);
+  // K stage 1 is read even when there is no tile 1: the registers then go
+  // unused (matrix half 0 computes no S^T).
+  preread(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
   softmax(rag == 0, t0 * BC);
-  __syncthreads();  // K stage 0 is free for tile 2
-  if (!grp_a) {     // group B starts half a step late
-    prefetch(std::integral_constant<int, 0>{}, 0);
-    __syncthreads();
+  __syncthreads();  // K stage 0 is free for tile S
+  if (!grp_a) {
+    if (S < tiles) fetch_k(0, (t0 + S) * BC, rag == S);
+    if (S - 1 < tiles) fetch_v(S - 1, (t0 + S - 1) * BC, rag == S - 1);
+    if (NW == 8) __syncthreads();  // group B starts half a step late
   }
 
-  using T0 = std::integral_constant<int, 0>;
-  using T1 = std::integral_constant<int, 1>;
+  using F0 = std::integral_constant<int, 0>;
+  using F1 = std::integral_constant<int, 1>;
+  using F2 = std::integral_constant<int, 2 % S>;
   const std::true_type Y;
   const std::false_type N;
+  // Steps in groups of S, so that stage offsets are immediates; the last
+  // step (no next tile: no S^T, no softmax) follows the loop.
   int t = 0;
-  for (; t + 2 < tiles; t += 2) {
-    step(Y, T0{}, t);
-    step(Y, T1{}, t + 1);
-  }
-  if (t + 1 < tiles) {
-    step(Y, T0{}, t);
-    step(N, T1{}, t + 1);
+  if constexpr (S == 3) {
+    for (; t + 3 < tiles; t += 3) {
+      step(Y, F0{}, t);
+      step(Y, F1{}, t + 1);
+      step(Y, F2{}, t + 2);
+    }
+    if (t + 1 == tiles) {
+      step(N, F0{}, t);
+    } else if (t + 2 == tiles) {
+      step(Y, F0{}, t);
+      step(N, F1{}, t + 1);
+    } else {
+      step(Y, F0{}, t);
+      step(Y, F1{}, t + 1);
+      step(N, F2{}, t + 2);
+    }
   } else {
-    step(N, T0{}, t);
+    for (; t + 2 < tiles; t += 2) {
+      step(Y, F0{}, t);
+      step(Y, F1{}, t + 1);
+    }
+    if (t + 1 < tiles) {
+      step(Y, F0{}, t);
+      step(N, F1{}, t + 1);
+    } else {
+      step(N, F0{}, t);
+    }
   }
   if (grp_a) __syncthreads();  // matches group B's extra barrier
   {  // add the partner half-wave's partial sum

@@ -42,6 +42,26 @@ def test_small_dense(dtype, d, N):
     assert_close("L", f64(lse), L_ref, tol_l)
 
 
+# Just past the sizes that run in 4-wave workgroups: the 8-wave (two wave
+# groups, three K/V stages) kernel over 33, 34 and 35 key tiles, so that its
+# loop ends in each of its three phases, with and without a ragged last tile.
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [2049, 2112, 2176, 2200])
+def test_dense_eight_wave_tails(dtype, d, N):
+    dev = device()
+    B, H = 1, 2
+    seed = 3000 * d + N + (0 if dtype == "bf16" else 70000)
+    announce(f"dense 8-wave tails {dtype} B={B} H={H} N={N} d={d} seed={seed}")
+    q, k, v = workloads.dense_inputs(B, H, N, d, dtype, seed=seed)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_dense(q, k, v, scale, dev)
+    O_ref, L_ref = oracle.attention_dense(q, k, v, scale)
+    tol_o, tol_l = TOL[dtype]
+    assert_close("O", f64(o), O_ref, tol_o)
+    assert_close("L", f64(lse), L_ref, tol_l)
+
+
 @pytest.mark.parametrize("name", ["single_head_fp32", "short_bf16", "large_logit_fp16_a",
                                   "large_logit_fp16_b"])
 def test_workload_full(name):
@@ -131,6 +151,28 @@ def test_small_varlen(dtype, d):
     tol_o, tol_l = TOL[dtype]
     assert_close("varlen O", f64(o), O_ref, tol_o)
     assert_close("varlen L", f64(lse), L_ref, tol_l)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_eight_wave_short_sequences(d):
+    # One sequence longer than the 4-wave limit puts the whole batch on the
+    # 8-wave kernel; the short ones then visit 1, 2 and 3 key tiles.
+    dev = device()
+    lengths = [1, 63, 64, 65, 130, 4160, 129, 2, 192, 150]
+    H = 2
+    announce(f"varlen 8-wave short sequences bf16 d={d} lengths={lengths}")
+    q, k, v, cu = workloads.varlen_inputs(lengths, H, d, "bf16", seed=d + 11)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_varlen(q, k, v, cu, max(lengths), scale, dev)
+    tol_o, tol_l = TOL["bf16"]
+    rng = np.random.default_rng(d)
+    for s, n in enumerate(lengths):
+        a = int(cu[s])
+        rows = np.arange(n) if n <= 256 else _sample_rows(n, rng, extra=16)
+        for h in range(H):
+            O_ref, L_ref = oracle.attention_varlen_rows(q, k, v, cu, scale, s, h, rows)
+            assert_close(f"varlen O[seq={s},h={h}]", f64(o[a + rows, h]), O_ref, tol_o)
+            assert_close(f"varlen L[seq={s},h={h}]", f64(lse[h, a + rows]), L_ref, tol_l)
 
 
 def test_varlen_with_empty_sequences():
