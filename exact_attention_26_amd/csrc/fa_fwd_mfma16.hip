@@ -140,8 +140,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   }
 
   // LDS holds S K stages followed by S V stages; tile j of either lives in
-  // stage j % S. K runs one tile ahead of V: the matrix half of step j reads
-  // K of tile j+1 (for S^T) and V of tile j (for P.V).
+  // stage (j + ph) % S (ph below). K runs one tile ahead of V: the matrix
+  // half of step j reads K of tile j+1 (for S^T) and V of tile j (for P.V).
   //
   // Direct-to-LDS copies: copy r of this wave fills bytes
   // [1024*(wave*NDMA + r), +1024) of a tile; lane i writes 16 bytes at
@@ -388,8 +388,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   i16x4 va[NB][2];
   // Operands of MFMA step i of a matrix half: the K chunk for S^T of the
   // next tile (K stage KS) and the transposed V rows for P.V (V stage VS).
-  auto read = [&](auto kstage, auto vstage, int i) __attribute__((always_inline)) {
-    constexpr int KS = decltype(kstage)::value, VS = decltype(vstage)::value;
+  auto read = [&](int KS, int VS, int i) __attribute__((always_inline)) {
     const int ss = i >> 1, kt = i & 1;
     ka[i % NB] = *(const __attribute__((address_space(3))) vec8*)(
         kp[ss] + KS * T::TILEB + kt * 32 * T::ROWB);
@@ -399,7 +398,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
       va[i % NB][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_i16x4*)(vp[dt] + VS * T::TILEB + (16 * t + 8 * h) * T::ROWB));
   };
-  auto preread = [&](auto kstage, auto vstage) __attribute__((always_inline)) {
+  auto preread = [&](int kstage, int vstage) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < AH; ++i) read(kstage, vstage, i);
   };
@@ -411,7 +410,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
     __builtin_amdgcn_s_setprio(FA_PP_PRIO);
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) {
-      if (i + AH < NSTEP) read(kstage, vstage, i + AH);
+      if (i + AH < NSTEP) read(decltype(kstage)::value, decltype(vstage)::value, i + AH);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (HN) {
         const int ss = i >> 1, kt = i & 1;
@@ -425,8 +424,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
     }
     __builtin_amdgcn_s_setprio(0);
   };
-  // Copies issued in the softmax half of step t: K of tile t+1+S into K
-  // stage (t+1) % S and V of tile t+S into V stage t % S. Both stages were
+  // Copies issued in the softmax half of step t (phase F): K of tile t+1+S
+  // into K stage (F+1) % S and V of tile t+S into V stage F. Both stages were
   // last read in the matrix halves of step t, which every wave has finished
   // at the barrier before. The copies complete (vmcnt(0)) at the end of the
   // issuing waves' next matrix half, before the barrier after which the
@@ -436,7 +435,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
     if (t + 1 + S < tiles) fetch_k(KS, (t0 + t + 1 + S) * BC, t + 1 + S == rag);
     if (t + S < tiles) fetch_v(VS, (t0 + t + S) * BC, t + S == rag);
   };
-  // Step t (F = t % S): [matrix(t)] | [softmax of tile t+1] |. With 8
+  // Step t (phase F = (t + ph) % S): [matrix(t)] | [softmax of tile t+1] |. With 8
   // waves, group B runs every step one half-step (one barrier) after group
   // A, so on each SIMD the matrix half of one wave meets the softmax half of
   // the other. Group B issues the copies. At the start of its softmax half
@@ -454,23 +453,37 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if constexpr (decltype(has_next)::value) {
-      preread(KN{}, VN{});
+      preread(KN::value, VN::value);
       if (!grp_a) copies(KS{}, VS{}, t);
       softmax(t + 1 == rag, (t0 + t + 1) * BC);
     }
     __syncthreads();
   };
 
+  // Tile j (visiting order) lives in stage (j + ph) % S; every step has a
+  // compile-time phase, so every stage offset is an immediate. With PEEL,
+  // the r = (tiles-1) % S steps that do not fill a group of S run before
+  // the loop, in phases S-r .. S-1, so that the loop runs whole groups in
+  // phases 0 .. S-1 and the last step (no next tile: no S^T, no softmax)
+  // has phase 0. Otherwise ph = 0 and the remainder follows the loop. A
+  // remainder after the loop spilled registers with three stages and with
+  // a band (measured: the spills cost HBM writes); with neither it is the
+  // faster of the two.
+  constexpr bool PEEL = S == 3 || BAND;
+  const int r = PEEL ? (tiles - 1) % S : 0;
+  const int ph = (S - r) % S;
+  auto stage_of = [&](int j) { return (j + ph) % S; };
+
   // Prologue: tiles 0 .. S-1 of K and 0 .. S-2 of V; S^T and softmax of tile
-  // 0; the first operands of matrix half 0 (K stage 1, V stage 0); then the
-  // copies that step -1 would have issued (K of tile S, V of tile S-1).
+  // 0; the first operands of matrix half 0 (K of tile 1, V of tile 0); then
+  // the copies that step -1 would have issued (K of tile S, V of tile S-1).
   if (!grp_a) {
 #pragma unroll
     for (int i = 0; i < S; ++i)
-      if (i < tiles) fetch_k(i, (t0 + i) * BC, rag == i);
+      if (i < tiles) fetch_k(stage_of(i), (t0 + i) * BC, rag == i);
 #pragma unroll
     for (int i = 0; i + 1 < S; ++i)
-      if (i < tiles) fetch_v(i, (t0 + i) * BC, rag == i);
+      if (i < tiles) fetch_v(stage_of(i), (t0 + i) * BC, rag == i);
   }
   // Consume Q here, after the first copies are issued, so its load latency
   // overlaps theirs and the compiler waits for these loads before the key
@@ -480,15 +493,18 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   for (int s = 0; s < D / 16; ++s) __asm__ volatile("" : : "v"(qf[s]));
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  qk(0, sc);
-  // K stage 1 is read even when there is no tile 1: the registers then go
-  // unused (matrix half 0 computes no S^T).
-  preread(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+  qk(stage_of(0), sc);
+  // The K stage of tile 1 is read even when there is no tile 1: the
+  // registers then go unused (matrix half 0 computes no S^T). The stage
+  // offsets are computed here, not chosen by a branch on ph: hipcc (ROCm
+  // 7.2) miscompiled a three-way branch with a constant-stage read in each
+  // arm (the ph == 2 arm read K through an address register it never set).
+  preread(stage_of(1), stage_of(0));
   softmax(rag == 0, t0 * BC);
-  __syncthreads();  // K stage 0 is free for tile S
+  __syncthreads();  // the K stage of tile 0 is free for tile S
   if (!grp_a) {
-    if (S < tiles) fetch_k(0, (t0 + S) * BC, rag == S);
-    if (S - 1 < tiles) fetch_v(S - 1, (t0 + S - 1) * BC, rag == S - 1);
+    if (S < tiles) fetch_k(stage_of(S), (t0 + S) * BC, rag == S);
+    if (S - 1 < tiles) fetch_v(stage_of(S - 1), (t0 + S - 1) * BC, rag == S - 1);
     if (NW == 8) __syncthreads();  // group B starts half a step late
   }
 
@@ -497,25 +513,18 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   using F2 = std::integral_constant<int, 2 % S>;
   const std::true_type Y;
   const std::false_type N;
-  // Steps in groups of S, so that stage offsets are immediates; the last
-  // step (no next tile: no S^T, no softmax) follows the loop.
   int t = 0;
-  if constexpr (S == 3) {
-    for (; t + 3 < tiles; t += 3) {
+  if constexpr (PEEL) {
+    if constexpr (S == 3) {
+      if (r == 2) step(Y, F1{}, t++);
+    }
+    if (r >= 1) step(Y, std::integral_constant<int, S - 1>{}, t++);
+    for (; t + 1 < tiles; t += S) {
       step(Y, F0{}, t);
       step(Y, F1{}, t + 1);
-      step(Y, F2{}, t + 2);
+      if constexpr (S == 3) step(Y, F2{}, t + 2);
     }
-    if (t + 1 == tiles) {
-      step(N, F0{}, t);
-    } else if (t + 2 == tiles) {
-      step(Y, F0{}, t);
-      step(N, F1{}, t + 1);
-    } else {
-      step(Y, F0{}, t);
-      step(Y, F1{}, t + 1);
-      step(N, F2{}, t + 2);
-    }
+    step(N, F0{}, t);
   } else {
     for (; t + 2 < tiles; t += 2) {
       step(Y, F0{}, t);

@@ -86,3 +86,10 @@ def test_seq_len_override_keeps_the_rest_of_the_workload():
     assert w["scale"] == base["scale"]
     with pytest.raises(ValueError):
         workloads.make("varlen_bf16", seq_len=96)
+
+
+def test_no_sampler_under_a_profiler(monkeypatch):
+    monkeypatch.setenv("ROCP_TOOL_LIBRARIES", "/opt/rocm/lib/rocprofiler-sdk/librocprofiler-sdk-tool.so")
+    monkeypatch.setattr(bench, "_sampler", None)
+    bench.start_sclk_sampler()
+    assert bench._sampler is None

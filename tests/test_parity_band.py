@@ -105,6 +105,26 @@ def test_full_size_banded_sampled(window):
         assert_close(f"L[b={b},h={h}]", f64(lse[b, h, rows]), L_ref, tol_l)
 
 
+# Windows above the 4-wave limit run the 8-wave kernel. With N = 6000 and
+# window 2100 its 256-row workgroups visit 37, 41, 45, ... key tiles, so the
+# loop starts in each of its three phases; near the end of the sequence the
+# visited range is cut by n and ends in a ragged tile.
+@pytest.mark.parametrize("d", [64, 128])
+def test_banded_eight_wave_phases(d):
+    dev = device()
+    B, H, N, window = 1, 2, 6000, 2100
+    announce(f"banded 8-wave phases bf16 B={B} H={H} N={N} d={d} window={window} (rows of every workgroup)")
+    q, k, v = workloads.dense_inputs(B, H, N, d, "bf16", seed=40 + d)
+    scale = 1.0 / math.sqrt(d)
+    o, lse = run_banded(q, k, v, window, scale, dev)
+    tol_o, tol_l = TOL["bf16"]
+    rows = np.unique(np.concatenate([np.arange(0, N, 37), np.arange(N - 300, N)]))
+    for h in range(H):
+        O_ref, L_ref = oracle.attention_banded_dense_rows(q, k, v, scale, window, 0, h, rows)
+        assert_close(f"O[h={h}]", f64(o[0, h, rows]), O_ref, tol_o)
+        assert_close(f"L[h={h}]", f64(lse[0, h, rows]), L_ref, tol_l)
+
+
 def test_banded_is_deterministic():
     dev = device()
     announce("banded determinism bf16 B=1 H=4 N=3000 d=128 window=200")
