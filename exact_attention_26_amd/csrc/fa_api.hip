@@ -74,8 +74,15 @@ int launch(const fa::FwdParams& p, int d, int dtype, bool varlen, void* stream,
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
-// Workgroups are 256 threads; keep the grid within 32-bit thread counts.
-constexpr int64_t kMaxBlocks = (int64_t{1} << 32) / 256 - 1;
+// A launch covers at most 2^32 - 1 work-items (workgroups x threads) in its
+// one grid dimension. Every kernel here runs 256-thread workgroups except the
+// 8-wave 16-bit forward (512); the fp32 forward's are 256.
+constexpr int64_t kMaxWorkItems = (int64_t{1} << 32) - 1;
+constexpr int kThreadsDefault = 256;
+constexpr int64_t kMaxBlocks = kMaxWorkItems / kThreadsDefault;
+bool grid_fits(int64_t blocks, int threads) { return blocks <= kMaxWorkItems / threads; }
+// Threads per workgroup of a forward launch with `waves` (fp32 runs 256).
+int fwd_threads(int dtype, int waves) { return dtype == FA_F32 ? kThreadsDefault : 64 * waves; }
 
 }  // namespace
 
@@ -92,7 +99,8 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B
   if ((int64_t)N * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
   const int waves = (dtype != FA_F32 && N <= kDenseNarrowMaxN) ? kWavesNarrow : kWavesPingPong;
   const int br = dtype == FA_F32 ? fa::kRowsPerBlockF32 : 32 * waves;
-  if ((int64_t)((N + br - 1) / br) * H * B > kMaxBlocks) return FA_ERR_SIZE;
+  if (!grid_fits((int64_t)((N + br - 1) / br) * H * B, fwd_threads(dtype, waves)))
+    return FA_ERR_SIZE;
   const uint64_t elems = (uint64_t)B * H * N * d;
   const int st = check_buffers(Q, K, V, O, L, elems * elem_bytes(dtype), (uint64_t)B * H * N * 4);
   if (st != FA_OK) return st;
@@ -132,7 +140,7 @@ int fa_fwd_banded(const void* Q, const void* K, const void* V, void* O, float* L
   const int wcap = window < N ? window : N;  // a window of N or more keeps every key
   const int waves = wcap <= kBandNarrowMax ? kWavesNarrow : kWavesPingPong;
   const int br = 32 * waves;
-  if ((int64_t)((N + br - 1) / br) * H * B > kMaxBlocks) return FA_ERR_SIZE;
+  if (!grid_fits((int64_t)((N + br - 1) / br) * H * B, 64 * waves)) return FA_ERR_SIZE;
   const uint64_t elems = (uint64_t)B * H * N * d;
   const int st = check_buffers(Q, K, V, O, L, elems * 2, (uint64_t)B * H * N * 4);
   if (st != FA_OK) return st;
@@ -171,7 +179,8 @@ int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L
   if ((int64_t)max_seqlen * H * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
   const int waves = (dtype != FA_F32 && max_seqlen <= kVarlenNarrowMaxN) ? kWavesNarrow : kWavesPingPong;
   const int br = dtype == FA_F32 ? fa::kRowsPerBlockF32 : 32 * waves;
-  if ((int64_t)((max_seqlen + br - 1) / br) * H * nseq > kMaxBlocks) return FA_ERR_SIZE;
+  if (!grid_fits((int64_t)((max_seqlen + br - 1) / br) * H * nseq, fwd_threads(dtype, waves)))
+    return FA_ERR_SIZE;
   if (!cu_seqlens) return FA_ERR_NULL;
   const uint64_t elems = (uint64_t)total_tokens * H * d;
   const int st =
@@ -385,7 +394,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: an output overlaps an input or the other output";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: the HIP runtime refused the kernel launch";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
-    case FA_ERR_SIZE: return "FA_ERR_SIZE: tensor too large for 32-bit in-head offsets";
+    case FA_ERR_SIZE: return "FA_ERR_SIZE: problem too large for 32-bit in-head offsets or one launch grid";
     case FA_ERR_ARG: return "FA_ERR_ARG: an argument outside its documented range";
     default: return "unknown fa_status";
   }

@@ -67,7 +67,7 @@ typedef enum {
   FA_ERR_ALIAS = -6,    /* an output overlaps an input or the other output   */
   FA_ERR_LAUNCH = -7,   /* the HIP runtime refused the kernel launch         */
   FA_ERR_SCALE = -8,    /* scale not finite or not > 0                       */
-  FA_ERR_SIZE = -9,     /* a tensor too large for 32-bit in-head offsets     */
+  FA_ERR_SIZE = -9,     /* too large for 32-bit in-head offsets or one grid  */
   FA_ERR_ARG = -10      /* an argument outside its documented range          */
 } fa_status;
 

@@ -72,6 +72,14 @@ def varlen(lib, Q=A, K=B_, V=C, O=D, L=E, cu=0x60000000, nseq=3, T=300, maxlen=2
     (dict(Q=A + 8), -5), (dict(O=D + 2), -5), (dict(L=E + 4), -5),
     (dict(O=A), -6), (dict(O=B_ + 64), -6), (dict(L=C + 16), -6), (dict(L=D), -6),
     (dict(N=1 << 25, d=64), -9),
+    # Grid size: 8-wave (512-thread) workgroups for N > 2048, 16 per head at
+    # N = 4096; 2^32 - 1 work-items allow 8388607 of them. One head fewer
+    # passes the size check and fails on the fake pointers' overlap instead.
+    (dict(B=524288, H=1, N=4096, d=64), -9),
+    (dict(B=524287, H=1, N=4096, d=64), -6),
+    # fp32: 256-thread workgroups of 128 rows.
+    (dict(B=524288, H=1, N=4096, d=64, dtype=fa.FA_F32), -9),
+    (dict(B=524287, H=1, N=4096, d=64, dtype=fa.FA_F32), -6),
 ])
 def test_dense_validation(lib, kw, status):
     assert dense(lib, **kw) == status
