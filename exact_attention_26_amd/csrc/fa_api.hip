@@ -179,7 +179,16 @@ int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L
   if ((int64_t)max_seqlen * H * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
   const int waves = (dtype != FA_F32 && max_seqlen <= kVarlenNarrowMaxN) ? kWavesNarrow : kWavesPingPong;
   const int br = dtype == FA_F32 ? fa::kRowsPerBlockF32 : 32 * waves;
-  if (!grid_fits((int64_t)((max_seqlen + br - 1) / br) * H * nseq, fwd_threads(dtype, waves)))
+  // Longest-first order (nseq <= 64): one workgroup per unit, at most
+  // floor(T / br) + nseq per head (each sequence adds less than one block to
+  // T / br), and at most the q_blocks of every sequence.
+  const int64_t qblk = (max_seqlen + br - 1) / br;
+  int64_t units = 0;
+  if (nseq <= fa::kLptMaxSeqs) {
+    units = total_tokens / br + nseq;
+    if (units > qblk * nseq) units = qblk * nseq;
+  }
+  if (!grid_fits(units > 0 ? units * H : qblk * H * nseq, fwd_threads(dtype, waves)))
     return FA_ERR_SIZE;
   if (!cu_seqlens) return FA_ERR_NULL;
   const uint64_t elems = (uint64_t)total_tokens * H * d;
@@ -206,10 +215,11 @@ int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L
   p.H = H;
   p.N = max_seqlen;
   p.total_tokens = total_tokens;
-  p.q_blocks = (max_seqlen + br - 1) / br;
+  p.q_blocks = (int)qblk;
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.window = -1;
+  p.units_per_head = (int)units;
   return launch(p, d, dtype, true, stream, waves);
 }
 

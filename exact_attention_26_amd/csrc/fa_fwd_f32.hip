@@ -184,7 +184,7 @@ hipError_t launch_fwd_f32(const FwdParams& p, int d, bool varlen, hipStream_t st
     fn = varlen ? (const void*)fwd_f32_kernel<64, true> : (const void*)fwd_f32_kernel<64, false>;
   else
     fn = varlen ? (const void*)fwd_f32_kernel<128, true> : (const void*)fwd_f32_kernel<128, false>;
-  const dim3 grid((unsigned)((int64_t)p.q_blocks * p.H * p.B));
+  const dim3 grid((unsigned)fwd_grid(p));
   const dim3 block(kThreads);
   FwdParams arg = p;
   void* args[] = {&arg};

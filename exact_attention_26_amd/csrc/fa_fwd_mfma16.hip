@@ -583,7 +583,7 @@ hipError_t launch_fwd_mfma16(const FwdParams& p, int d, bool bf16, bool varlen, 
     fn = (d == 64) ? pick<true, 64>(varlen, band, waves) : pick<true, 128>(varlen, band, waves);
   else
     fn = (d == 64) ? pick<false, 64>(varlen, band, waves) : pick<false, 128>(varlen, band, waves);
-  const dim3 grid((unsigned)((int64_t)p.q_blocks * p.H * p.B));
+  const dim3 grid((unsigned)fwd_grid(p));
   const dim3 block(64 * waves);
   FwdParams arg = p;
   void* args[] = {&arg};

@@ -34,7 +34,19 @@ struct FwdParams {
   float scale_log2;           // scale * log2(e): exp(x*scale) = exp2(x*scale_log2)
   int window;                 // banded (dense 16-bit only): row r sees keys |r - c| <= window,
                               // 0 <= window <= N; -1 = every key
+  int units_per_head;         // varlen: > 0 runs each head's units longest sequence
+                              // first, this many workgroups per head (at least the
+                              // head's units); 0 = one workgroup per (block, seq, head)
 };
+
+// Packed batches of at most this many sequences take the longest-first order.
+constexpr int kLptMaxSeqs = 64;
+
+// Workgroups of one forward launch.
+inline int64_t fwd_grid(const FwdParams& p) {
+  return p.units_per_head > 0 ? (int64_t)p.units_per_head * p.H
+                              : (int64_t)p.q_blocks * p.H * p.B;
+}
 
 // Launchers; return 0 on success or a hipError_t from the launch.
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool varlen, hipStream_t stream);
