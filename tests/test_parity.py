@@ -215,3 +215,90 @@ def test_long_single_head_sampled():
     O_ref, L_ref = oracle.attention_dense_rows(q, k, v, 1.0 / math.sqrt(d), 0, 0, rows)
     assert_close("O", f64(o[0, 0, rows]), O_ref, TOL["bf16"][0])
     assert_close("L", f64(lse[0, 0, rows]), L_ref, TOL["bf16"][1])
+
+
+@pytest.mark.parametrize("nseq", [40, 80])
+def test_varlen_unit_order_with_ties(nseq):
+    # Up to 64 sequences run their units longest sequence first, ranked in
+    # the kernel (ties by index); more sequences keep the plain order. Both
+    # with many equal lengths, empty sequences and ragged tails.
+    dev = device()
+    rng = np.random.default_rng(nseq)
+    lengths = [int(x) for x in rng.choice([0, 1, 64, 65, 130, 200, 257], size=nseq)]
+    announce(f"varlen unit order nseq={nseq} bf16 d=64 lengths={lengths}")
+    q, k, v, cu = workloads.varlen_inputs(lengths, 2, 64, "bf16", seed=nseq)
+    o, lse = run_varlen(q, k, v, cu, max(lengths), 0.125, dev)
+    O_ref, L_ref = oracle.attention_varlen(q, k, v, cu, 0.125)
+    assert_close("varlen O", f64(o), O_ref, TOL["bf16"][0])
+    assert_close("varlen L", f64(lse), L_ref, TOL["bf16"][1])
+
+
+def test_varlen_sequence_longer_than_max_seqlen():
+    # max_seqlen sizes the grid: a longer sequence gets its first rows (up to
+    # max_seqlen, rounded up to a query block of at most 256 rows) computed
+    # against all of its keys; the rows past that block stay unwritten.
+    dev = device()
+    lengths, max_seqlen = [700, 90, 5], 100
+    announce(f"varlen lengths={lengths} with max_seqlen={max_seqlen}")
+    q, k, v, cu = workloads.varlen_inputs(lengths, 2, 128, "bf16", seed=31)
+    import exact_attention_26_amd as fa
+    T = sum(lengths)
+    o = torch.full((T, 2, 128), 7.0, dtype=torch.bfloat16, device=dev)
+    lse = torch.full((2, T), 7.0, dtype=torch.float32, device=dev)
+    fa.forward_varlen(q.to(dev), k.to(dev), v.to(dev), cu.to(dev), max_seqlen, 0.1, out=o, lse=lse)
+    torch.cuda.synchronize()
+    O_ref, L_ref = oracle.attention_varlen(q, k, v, cu, 0.1)
+    for s, n in enumerate(lengths):
+        a, done = int(cu[s]), min(n, max_seqlen)
+        assert_close(f"O seq {s}", f64(o[a:a + done]), O_ref[a:a + done], TOL["bf16"][0])
+        assert_close(f"L seq {s}", f64(lse[:, a:a + done]), L_ref[:, a:a + done], TOL["bf16"][1])
+    untouched = f64(o[256:700])
+    assert (untouched == 7.0).all() and (f64(lse[:, 256:700]) == 7.0).all()
+
+
+def test_dense_offsets_beyond_2_31_elements():
+    # 2^31 elements per tensor (4 GiB): the last heads start past 2^31, which
+    # only the 64-bit head bases reach. Q = K = V (allowed), sampled rows.
+    dev = device()
+    B, H, N, d = 1, 2049, 8192, 128
+    announce(f"dense offsets past 2^31 elements bf16 B={B} H={H} N={N} d={d} (sampled)")
+    x = workloads.device_normal((B, H, N, d), "bf16", seed=41, device=dev)
+    import exact_attention_26_amd as fa
+    o, lse = fa.forward(x, x, x, 1.0 / math.sqrt(d))
+    torch.cuda.synchronize()
+    assert (H - 1) * N * d >= 1 << 31
+    rows = _sample_rows(N, np.random.default_rng(41), extra=4)
+    for h in (0, H - 1):
+        xh = x[0, h].cpu()
+        O_ref, L_ref = oracle.attention_dense_rows(xh[None, None], xh[None, None], xh[None, None],
+                                                   1.0 / math.sqrt(d), 0, 0, rows)
+        assert_close(f"O h={h}", f64(o[0, h, rows]), O_ref, TOL["bf16"][0])
+        assert_close(f"L h={h}", f64(lse[0, h, rows]), L_ref, TOL["bf16"][1])
+
+
+@pytest.mark.parametrize("nseq", [64, 130])
+def test_varlen_offsets_beyond_2_31_elements(nseq):
+    # Packed [T, 16, 128] with T*H*d > 2^31: the last sequences start past
+    # 2^31 elements. 64 sequences take the longest-first order, 130 the plain
+    # one. Q = K = V (allowed), sampled rows of the first and last sequence.
+    dev = device()
+    H, d = 16, 128
+    base = (1 << 31) // (H * d) // (nseq - 1) + 64
+    lengths = [base + 64 * (i % 3) for i in range(nseq)]
+    T = sum(lengths)
+    announce(f"varlen offsets past 2^31 elements bf16 nseq={nseq} T={T} H={H} d={d} (sampled)")
+    assert (T - lengths[-1]) * H * d >= 1 << 31
+    x = workloads.device_normal((T, H, d), "bf16", seed=43, device=dev)
+    cu = workloads.cu_seqlens_of(lengths)
+    o, lse = run_varlen(x, x, x, cu, max(lengths), 1.0 / math.sqrt(d), dev)
+    rng = np.random.default_rng(43)
+    for s in (0, nseq - 1):
+        a, n = int(cu[s]), lengths[s]
+        rows = _sample_rows(n, rng, extra=4)
+        for h in (0, H - 1):
+            xs = x[a:a + n, h].cpu()
+            O_ref, L_ref = oracle.attention_dense_rows(xs[None, None], xs[None, None],
+                                                       xs[None, None], 1.0 / math.sqrt(d), 0, 0,
+                                                       rows)
+            assert_close(f"O seq {s} h={h}", f64(o[a + rows, h]), O_ref, TOL["bf16"][0])
+            assert_close(f"L seq {s} h={h}", f64(lse[h, a + rows]), L_ref, TOL["bf16"][1])

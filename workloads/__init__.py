@@ -120,6 +120,16 @@ def cu_seqlens_of(lengths) -> torch.Tensor:
     return torch.from_numpy(cu.astype(np.int32))
 
 
+def device_normal(shape, dtype: str, seed: int, device) -> torch.Tensor:
+    """N(0, 1) values of the storage dtype drawn on `device` by torch's seeded
+    device generator: inputs of several GiB that a host draw would take
+    minutes to make. The oracle side reads the same values back."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp16": torch.float16}[dtype]
+    return torch.randn(tuple(shape), generator=g, device=device, dtype=tdt)
+
+
 def varlen_inputs(lengths, H: int, d: int, dtype: str, seed: int = 0,
                   rng: np.random.Generator | None = None):
     """Packed [T,H,d] Q, K, V and int32 cu_seqlens for the given lengths.
