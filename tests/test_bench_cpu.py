@@ -59,6 +59,34 @@ def test_clock_sampler_protocol(tmp_path, monkeypatch):
     assert mhz == pytest.approx(2000.0) and watts == pytest.approx(1300.0)  # MEM clock excluded
 
 
+def test_clock_sampler_median_ignores_one_dip(tmp_path, monkeypatch):
+    # Five amd-smi samples; the second reads a throttling dip. Each sample is
+    # the mean over the GFX domains; the reported figure is their median.
+    count = tmp_path / "n"
+    count.write_text("0")
+    fake = tmp_path / "amd-smi"
+    fake.write_text(
+        "#!/bin/sh\n"
+        f"n=$(cat {count}); echo $((n + 1)) > {count}\n"
+        "if [ \"$n\" = 1 ]; then c0=900; c1=1100; w=700; else c0=1800; c1=1600; w=1350; fi\n"
+        "echo '    GFX_0:'; echo \"        CLK: $c0 MHz\"; echo '    GFX_1:'\n"
+        "echo \"        CLK: $c1 MHz\"; echo '    MEM_0:'; echo '        CLK: 1300 MHz'\n"
+        "echo \"    SOCKET_POWER: $w W\"\n")
+    fake.chmod(0o755)
+    monkeypatch.setenv("PATH", f"{tmp_path}:{os.environ['PATH']}")
+    import torch
+    monkeypatch.setattr(torch.cuda, "synchronize", lambda *a, **k: None)
+    bench.start_sclk_sampler()
+    try:
+        mhz, watts = bench.sample_sclk(lambda: None, seconds=0.2)
+    finally:
+        bench._sampler.stdin.close()
+        bench._sampler.wait(timeout=10)
+        bench._sampler = None
+    assert int(count.read_text()) == 5
+    assert mhz == pytest.approx(1700.0) and watts == pytest.approx(1350.0)
+
+
 def test_sampler_absent_gives_nulls(monkeypatch):
     monkeypatch.setattr(bench, "_sampler", None)
     assert bench.sample_sclk(lambda: None, seconds=0.0) == (None, None)
