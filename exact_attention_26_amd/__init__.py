@@ -170,19 +170,45 @@ def _require(cond: bool, msg: str) -> None:
         raise ValueError(msg)
 
 
+def _inputs_on_one_gpu(*ts) -> None:
+    """Every input tensor a kernel reads: a contiguous tensor on one GPU (a host
+    or another device's address would be dereferenced as this GPU's memory)."""
+    _require(all(t.is_cuda for t in ts), "inputs must be GPU tensors")
+    _require(len({t.device for t in ts}) == 1, "inputs must be on the same GPU")
+    _require(all(t.is_contiguous() for t in ts), "inputs must be contiguous")
+
+
+def _check_buffer(t, shape, dtype, device, name: str):
+    """A caller-supplied output or scratch buffer. The kernels write exactly
+    `shape` elements of `dtype` through its address, so a smaller, strided,
+    differently typed or foreign-device buffer is rejected rather than
+    overrun."""
+    _require(t.is_cuda and t.device == device, f"{name} must be on {device}")
+    _require(tuple(t.shape) == tuple(shape),
+             f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    _require(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+    return t
+
+
+def _out_or_new(t, shape, dtype, device, name: str):
+    import torch
+    if t is None:
+        return torch.empty(tuple(shape), dtype=dtype, device=device)
+    return _check_buffer(t, shape, dtype, device, name)
+
+
 def forward(q, k, v, scale: float | None = None, out=None, lse=None):
     """Dense forward on contiguous [B, H, N, d] tensors; returns (o, lse[B,H,N] fp32)."""
     import torch
     _require(q.dim() == 4 and q.shape == k.shape == v.shape, "q, k, v must share shape [B,H,N,d]")
     _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
-    _require(q.is_cuda and k.is_cuda and v.is_cuda, "q, k, v must be GPU tensors")
-    _require(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(),
-             "q, k, v must be contiguous")
+    _inputs_on_one_gpu(q, k, v)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if out is None else out
-    L = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = _out_or_new(out, q.shape, q.dtype, q.device, "out")
+    L = _out_or_new(lse, (B, H, N), torch.float32, q.device, "lse")
     fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), L.data_ptr(), B, H, N, d,
            scale, _dtype_code(q), _stream_handle(q.device))
     return o, L
@@ -194,14 +220,12 @@ def forward_banded(q, k, v, window: int, scale: float | None = None, out=None, l
     import torch
     _require(q.dim() == 4 and q.shape == k.shape == v.shape, "q, k, v must share shape [B,H,N,d]")
     _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
-    _require(q.is_cuda and k.is_cuda and v.is_cuda, "q, k, v must be GPU tensors")
-    _require(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(),
-             "q, k, v must be contiguous")
+    _inputs_on_one_gpu(q, k, v)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if out is None else out
-    L = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = _out_or_new(out, q.shape, q.dtype, q.device, "out")
+    L = _out_or_new(lse, (B, H, N), torch.float32, q.device, "lse")
     fa_fwd_banded(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), L.data_ptr(), B, H, N,
                   d, window, scale, _dtype_code(q), _stream_handle(q.device))
     return o, L
@@ -215,16 +239,13 @@ def forward_kv_outer(q, k, v, q_groups: int = 16, scale: float | None = None, ou
     import torch
     _require(q.dim() == 4 and q.shape == k.shape == v.shape, "q, k, v must share shape [B,H,N,d]")
     _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
-    _require(q.is_cuda and k.is_cuda and v.is_cuda, "q, k, v must be GPU tensors")
-    _require(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(),
-             "q, k, v must be contiguous")
+    _inputs_on_one_gpu(q, k, v)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if out is None else out
-    L = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
-    if acc is None:
-        acc = torch.empty(B * H * N * (d + 2), dtype=torch.float32, device=q.device)
+    o = _out_or_new(out, q.shape, q.dtype, q.device, "out")
+    L = _out_or_new(lse, (B, H, N), torch.float32, q.device, "lse")
+    acc = _out_or_new(acc, (B * H * N * (d + 2),), torch.float32, q.device, "acc")
     fa_fwd_kv_outer(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), L.data_ptr(),
                     acc.data_ptr(), B, H, N, d, q_groups, scale, _dtype_code(q),
                     _stream_handle(q.device))
@@ -238,17 +259,15 @@ def forward_varlen(q, k, v, cu_seqlens, max_seqlen: int, scale: float | None = N
     import torch
     _require(q.dim() == 3 and q.shape == k.shape == v.shape, "q, k, v must share shape [T,H,d]")
     _require(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
-    _require(q.is_cuda and cu_seqlens.is_cuda, "q, k, v, cu_seqlens must be GPU tensors")
     _require(cu_seqlens.dtype == torch.int32 and cu_seqlens.dim() == 1,
              "cu_seqlens must be a 1-D int32 tensor")
-    _require(q.is_contiguous() and k.is_contiguous() and v.is_contiguous()
-             and cu_seqlens.is_contiguous(), "inputs must be contiguous")
+    _inputs_on_one_gpu(q, k, v, cu_seqlens)
     T, H, d = q.shape
     nseq = cu_seqlens.numel() - 1
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    o = torch.empty_like(q) if out is None else out
-    L = torch.empty((H, T), dtype=torch.float32, device=q.device) if lse is None else lse
+    o = _out_or_new(out, q.shape, q.dtype, q.device, "out")
+    L = _out_or_new(lse, (H, T), torch.float32, q.device, "lse")
     fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), L.data_ptr(),
                   cu_seqlens.data_ptr(), nseq, T, int(max_seqlen), H, d, scale, _dtype_code(q),
                   _stream_handle(q.device))
@@ -264,17 +283,16 @@ def backward(q, k, v, o, do, lse, scale: float | None = None, dq=None, dk=None, 
              "q, k, v, o, do must share shape [B,H,N,d]")
     _require(q.dtype == k.dtype == v.dtype == o.dtype == do.dtype,
              "q, k, v, o, do must share a dtype")
-    _require(all(t.is_cuda and t.is_contiguous() for t in (q, k, v, o, do, lse)),
-             "inputs must be contiguous GPU tensors")
+    _inputs_on_one_gpu(q, k, v, o, do, lse)
     B, H, N, d = q.shape
     _require(lse.dtype == torch.float32 and tuple(lse.shape) == (B, H, N),
              "lse must be float32 [B,H,N]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
+    dq = _out_or_new(dq, q.shape, q.dtype, q.device, "dq")
+    dk = _out_or_new(dk, q.shape, q.dtype, q.device, "dk")
+    dv = _out_or_new(dv, q.shape, q.dtype, q.device, "dv")
+    delta = _out_or_new(delta, (B, H, N), torch.float32, q.device, "delta")
     fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(), lse.data_ptr(),
            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), B, H, N, d, scale,
            _dtype_code(q), _stream_handle(q.device))
@@ -299,9 +317,23 @@ def dropout_add_norm(x0, gamma0, beta0=None, residual=None, x1=None, gamma1=None
     _require(all(t.shape == x0.shape for t in ts), "x0, x1, residual must share a shape")
     _require(all(t.numel() == hidden for t in ws), "gamma/beta must have `hidden` elements")
     _require(all(t.dtype == x0.dtype for t in ts + ws), "all tensors must share a dtype")
-    _require(all(t.is_cuda and t.is_contiguous() for t in ts + ws),
-             "inputs must be contiguous GPU tensors")
+    _inputs_on_one_gpu(*ts, *ws)
     if out is not None:
+        # The same outputs a call with these arguments allocates, and no others:
+        # the kernel writes each non-null one and skips the null ones.
+        want = {"y0": (x0.shape, x0.dtype), "y1": (x0.shape, x0.dtype) if gamma1 is not None else None,
+                "z": (x0.shape, x0.dtype) if prenorm else None,
+                "mean": ((rows,), torch.float32) if stats and not rms else None,
+                "rstd": ((rows,), torch.float32) if stats else None,
+                "mask": ((2 if x1 is not None else 1, rows, hidden), torch.uint8)
+                if return_mask else None}
+        for name, spec in want.items():
+            t = out.get(name)
+            if spec is None:
+                _require(t is None, f"out[{name!r}] must be None for these arguments")
+            else:
+                _require(t is not None, f"out[{name!r}] is missing")
+                _check_buffer(t, spec[0], spec[1], x0.device, f"out[{name!r}]")
         o = out
         fa_dropout_add_norm(*(None if t is None else t.data_ptr() for t in
                               (x0, x1, residual, gamma0, beta0, gamma1, beta1, o["y0"], o["y1"],
