@@ -101,8 +101,10 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
  *                  caller's responsibility: they are read on the device and
  *                  not checked.
  *   max_seqlen   : host-side upper bound of every sequence length; it sizes
- *                  the grid. Rows of a longer sequence beyond max_seqlen are
- *                  not written. max_seqlen*H*d must be below 2^31.
+ *                  the grid. Of a longer sequence, the first max_seqlen rows
+ *                  are computed (against all of its keys), and the rows past
+ *                  max_seqlen rounded up to the kernel's query block (128 or
+ *                  256 rows) are not written. max_seqlen*H*d must be below 2^31.
  * Returns an fa_status.
  */
 int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L,
