@@ -153,18 +153,19 @@ def test_small_varlen(dtype, d):
     assert_close("varlen L", f64(lse), L_ref, tol_l)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
 @pytest.mark.parametrize("d", [64, 128])
-def test_varlen_eight_wave_short_sequences(d):
+def test_varlen_eight_wave_short_sequences(dtype, d):
     # One sequence longer than the 4-wave limit puts the whole batch on the
     # 8-wave kernel; the short ones then visit 1, 2 and 3 key tiles.
     dev = device()
     lengths = [1, 63, 64, 65, 130, 4160, 129, 2, 192, 150]
     H = 2
-    announce(f"varlen 8-wave short sequences bf16 d={d} lengths={lengths}")
-    q, k, v, cu = workloads.varlen_inputs(lengths, H, d, "bf16", seed=d + 11)
+    announce(f"varlen 8-wave short sequences {dtype} d={d} lengths={lengths}")
+    q, k, v, cu = workloads.varlen_inputs(lengths, H, d, dtype, seed=d + 11)
     scale = 1.0 / math.sqrt(d)
     o, lse = run_varlen(q, k, v, cu, max(lengths), scale, dev)
-    tol_o, tol_l = TOL["bf16"]
+    tol_o, tol_l = TOL[dtype]
     rng = np.random.default_rng(d)
     for s, n in enumerate(lengths):
         a = int(cu[s])
