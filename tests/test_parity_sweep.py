@@ -1,4 +1,5 @@
-"""Seeded random sweep of the forward entry points against the float64 oracle:
+"""Seeded random sweep of the dense, packed and banded forwards and the backward
+against the float64 oracles:
 random storage dtypes, head sizes, batch and head counts, ragged lengths,
 scales and packed-sequence mixes, drawn once from a fixed seed so every run
 checks the same cases. It crosses the 4-/8-wave threshold of the dense
@@ -79,3 +80,61 @@ def test_varlen_sweep(case):
     tol_o, tol_l = TOL[dtype]
     assert_close("O", f64(o), O_ref, tol_o)
     assert_close("L", f64(lse), L_ref, tol_l)
+
+
+def _band_cases(n=12, seed=2028):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = ["bf16", "fp16"][rng.integers(2)]
+        d = [64, 128][rng.integers(2)]
+        if rng.random() < 0.3:  # windows past 2048 take the 8-wave kernel
+            N, window = int(rng.integers(2100, 2600)), int(rng.integers(2049, 2600))
+        else:
+            N = int(rng.integers(1, 500))
+            window = int(rng.choice([0, 1, 31, 63, 64, 65, int(rng.integers(0, 600))]))
+        cases.append((i, dtype, d, int(rng.integers(1, 3)), int(rng.integers(1, 3)), N, window,
+                      float(rng.uniform(0.05, 0.3))))
+    return cases
+
+
+@pytest.mark.parametrize("case", _band_cases(), ids=lambda c: f"band{c[0]}-{c[1]}-d{c[2]}-N{c[5]}-w{c[6]}")
+def test_banded_sweep(case):
+    import exact_attention_26_amd as fa
+    i, dtype, d, B, H, N, window, scale = case
+    dev = device()
+    announce(f"sweep banded #{i}: {dtype} B={B} H={H} N={N} d={d} window={window} scale={scale:.4f}")
+    q, k, v = workloads.dense_inputs(B, H, N, d, dtype, seed=3000 + i)
+    o, lse = fa.forward_banded(q.to(dev), k.to(dev), v.to(dev), window, scale)
+    tol_o, tol_l = TOL[dtype]
+    if N <= 500:
+        O_ref, L_ref = oracle.attention_banded_dense(q, k, v, scale, window)
+        assert_close("O", f64(o), O_ref, tol_o)
+        assert_close("L", f64(lse), L_ref, tol_l)
+        return
+    rng = np.random.default_rng(i)
+    rows = np.unique(np.concatenate([[0, 255, 256, N // 2, N - 257, N - 1],
+                                     rng.integers(0, N, size=12)]))
+    for b, h in {(0, 0), (B - 1, H - 1)}:
+        O_ref, L_ref = oracle.attention_banded_dense_rows(q, k, v, scale, window, b, h, rows)
+        assert_close(f"O[{b},{h}]", f64(o[b, h, rows]), O_ref, tol_o)
+        assert_close(f"L[{b},{h}]", f64(lse[b, h, rows]), L_ref, tol_l)
+
+
+def _bwd_cases(n=12, seed=2029):
+    rng = np.random.default_rng(seed)
+    return [(i, ["bf16", "fp16"][rng.integers(2)], [64, 128][rng.integers(2)],
+             int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.integers(1, 700)),
+             float(rng.uniform(0.05, 0.3))) for i in range(n)]
+
+
+@pytest.mark.parametrize("case", _bwd_cases(), ids=lambda c: f"bwd{c[0]}-{c[1]}-d{c[2]}-N{c[5]}")
+def test_backward_sweep(case):
+    from test_parity_bwd import TOL_BWD, check_grads, run_bwd
+    i, dtype, d, B, H, N, scale = case
+    dev = device()
+    announce(f"sweep backward #{i}: {dtype} B={B} H={H} N={N} d={d} scale={scale:.4f}")
+    q, k, v, do = workloads.dense_bwd_inputs(B, H, N, d, dtype, seed=4000 + i)
+    got = run_bwd(q, k, v, do, scale, dev)
+    want = oracle.attention_backward_dense(q, k, v, do, scale)
+    check_grads(f"sweep {i}", got, want, TOL_BWD[dtype])
