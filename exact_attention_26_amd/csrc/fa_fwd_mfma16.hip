@@ -339,16 +339,29 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   auto softmax = [&](bool ragged, int kb) __attribute__((always_inline)) {
     if (ragged || band_edge(kb)) mask(sc, kb);
     f32x16 pf[2];
+    // Three groups fenced apart: the 32 exponent arguments, the 32
+    // exponentials, then the sums. Left to itself the compiler puts each
+    // exponential's consumer right behind it, where it waits for the
+    // transcendental unit; grouped, no instruction waits on a result still
+    // in flight (measured 0.7-1.2 % faster on the whole kernel).
     auto exps = [&]() {
       const float mc = m * c2;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pf[kt][i] = fmaf(sc[kt][i], c2, -mc);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) pf[kt][i] = __builtin_amdgcn_exp2f(pf[kt][i]);
+      __builtin_amdgcn_sched_barrier(0);
       float ls[4];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          pf[kt][i] = __builtin_amdgcn_exp2f(fmaf(sc[kt][i], c2, -mc));
+        for (int i = 0; i < 16; ++i)
           ls[i & 3] = (kt == 0 && i < 4) ? pf[kt][i] : ls[i & 3] + pf[kt][i];
-        }
       return (ls[0] + ls[1]) + (ls[2] + ls[3]);
     };
     float lsum = exps();
