@@ -219,19 +219,30 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // Exponent arguments, exponentials, then dS, as three fenced groups so
+      // that no instruction waits right behind the exponential it consumes.
       float pr[16], ds[16];
+      f32x4 dvq[4];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int qi = hq * 32 + 8 * a + 4 * g;
         const f32x4 lv = *(const f32x4*)(Ls + qi);
-        const f32x4 dv4 = *(const f32x4*)(Ds + qi);
+        dvq[a] = *(const f32x4*)(Ds + qi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pr[4 * a + e] = fmaf(s[4 * a + e], c2, -lv[e] * kLog2e);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) pr[i] = __builtin_amdgcn_exp2f(pr[i]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int qi = hq * 32 + 8 * a + 4 * g;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * a + e;
-          float x = __builtin_amdgcn_exp2f(fmaf(s[i], c2, -lv[e] * kLog2e));
-          if (q0 + qi + e >= n) x = 0.f;  // query past the end
-          pr[i] = x;
-          ds[i] = x * (dp[i] - dv4[e]);
+          if (q0 + qi + e >= n) pr[i] = 0.f;  // query past the end
+          ds[i] = pr[i] * (dp[i] - dvq[a][e]);
         }
       }
       // P and dS as B operands: slot jj of lane group g in product t is
@@ -390,26 +401,39 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2))) 
         dp[kt] = mfma32x32x16<BF16>(va, of[ss], dp[kt]);
       }
     const bool ragged = k0 + TK > n;
+    // P^T then dS^T, one 32-key half at a time: the half's exponent arguments,
+    // its exponentials, then its dS, as three fenced groups, so no instruction
+    // waits right behind the exponential it consumes.
     vec8 pb[4];  // dS^T as B operands, 16 keys each (as the forward packs P)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      u32x4 w;
+    for (int kt = 0; kt < 2; ++kt) {
+      f32x16 pe;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float x[2];
+      for (int i = 0; i < 16; ++i) pe[i] = fmaf(s[kt][i], c2, -lq);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int i = 8 * (t & 1) + 2 * q + e;
-          float pv = __builtin_amdgcn_exp2f(fmaf(s[t >> 1][i], c2, -lq));
-          if (ragged) {
-            const int key = k0 + (t >> 1) * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key >= n) pv = 0.f;
+      for (int i = 0; i < 16; ++i) pe[i] = __builtin_amdgcn_exp2f(pe[i]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        u32x4 w;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float x[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int i = 8 * h + 2 * q + e;
+            float pv = pe[i];
+            if (ragged) {
+              const int key = k0 + kt * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
+              if (key >= n) pv = 0.f;
+            }
+            x[e] = pv * (dp[kt][i] - dq_d);
           }
-          x[e] = pv * (dp[t >> 1][i] - dq_d);
+          w[q] = pack2<BF16>(x[0], x[1]);
         }
-        w[q] = pack2<BF16>(x[0], x[1]);
+        pb[2 * kt + h] = __builtin_bit_cast(vec8, w);
       }
-      pb[t] = __builtin_bit_cast(vec8, w);
     }
 #pragma unroll
     for (int t = 0; t < 4; ++t)
@@ -439,8 +463,12 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2))) 
     __syncthreads();
   }
 
-  if (qr < n) {
-    unsigned short* row = (unsigned short*)p.dq + hb + (int64_t)qr * D;
+  // The query row again, from the lane count rather than the thread index, so
+  // that no per-lane address stays live (and spills) across the key loop.
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int qr_e = qb * kBwdQueriesPerBlock + wave * 32 + (lane_e & 31);
+  if (qr_e < n) {
+    unsigned short* row = (unsigned short*)p.dq + hb + (int64_t)qr_e * D;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
