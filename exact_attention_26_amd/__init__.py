@@ -42,6 +42,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+import threading
 
 __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "LIB_PATH", "load", "fa_fwd", "fa_fwd_varlen",
@@ -62,6 +63,7 @@ EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_banded", "fa_fwd_kv_outer
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 _lib = None
+_lib_lock = threading.Lock()
 
 
 class FaError(RuntimeError):
@@ -72,10 +74,15 @@ class FaError(RuntimeError):
 
 
 def load() -> ctypes.CDLL:
-    """Load libfa.so once and declare its C signatures."""
-    global _lib
+    """Load libfa.so once and declare its C signatures (thread-safe)."""
     if _lib is not None:
         return _lib
+    with _lib_lock:
+        return _lib if _lib is not None else _load_locked()
+
+
+def _load_locked() -> ctypes.CDLL:
+    global _lib
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_attention_26_amd.build`")
     lib = ctypes.CDLL(LIB_PATH)
