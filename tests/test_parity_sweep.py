@@ -5,8 +5,10 @@ scales and packed-sequence mixes, drawn once from a fixed seed so every run
 checks the same cases. It crosses the 4-/8-wave threshold of the dense
 16-bit path (N = 2048) and the 64-sequence threshold of the packed unit order.
 Full comparison for short problems, sampled rows (exact against all keys)
-for long ones."""
+for long ones. FA_SWEEP_MULT=k draws k times as many cases per kernel (the
+default set is the first of them); the default is 1."""
 import math
+import os
 
 import numpy as np
 import pytest
@@ -16,9 +18,10 @@ import workloads
 from gpu_helpers import TOL, announce, assert_close, device, f64, run_dense, run_varlen
 
 pytestmark = pytest.mark.gpu
+MULT = max(1, int(os.environ.get("FA_SWEEP_MULT", "1")))
 
 
-def _dense_cases(n=24, seed=2026):
+def _dense_cases(n=24 * MULT, seed=2026):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -31,7 +34,7 @@ def _dense_cases(n=24, seed=2026):
     return cases
 
 
-def _varlen_cases(n=12, seed=2027):
+def _varlen_cases(n=12 * MULT, seed=2027):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -82,7 +85,7 @@ def test_varlen_sweep(case):
     assert_close("L", f64(lse), L_ref, tol_l)
 
 
-def _band_cases(n=12, seed=2028):
+def _band_cases(n=12 * MULT, seed=2028):
     rng = np.random.default_rng(seed)
     cases = []
     for i in range(n):
@@ -121,7 +124,7 @@ def test_banded_sweep(case):
         assert_close(f"L[{b},{h}]", f64(lse[b, h, rows]), L_ref, tol_l)
 
 
-def _bwd_cases(n=12, seed=2029):
+def _bwd_cases(n=12 * MULT, seed=2029):
     rng = np.random.default_rng(seed)
     return [(i, ["bf16", "fp16"][rng.integers(2)], [64, 128][rng.integers(2)],
              int(rng.integers(1, 3)), int(rng.integers(1, 3)), int(rng.integers(1, 700)),
