@@ -33,6 +33,8 @@ constexpr int kWavesNarrow = 4;
 constexpr int kBandNarrowMax = FA_BAND_NARROW_MAX;     // windows (capped at N)
 constexpr int kDenseNarrowMaxN = FA_DENSE_NARROW_MAX_N;
 constexpr int kVarlenNarrowMaxN = FA_VARLEN_NARROW_MAX_N;  // max_seqlen
+// Largest query block of any forward kernel (the 8-wave 16-bit one).
+constexpr int kMaxRowsPerBlock = 256;
 
 constexpr int kVersion = 500;  // 0.5.0: adds fa_dropout_add_norm
 
@@ -176,7 +178,11 @@ int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
   if (nseq == 0 || total_tokens == 0 || max_seqlen == 0 || H == 0) return FA_OK;
 
-  if ((int64_t)max_seqlen * H * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
+  // Query rows run up to max_seqlen rounded up to a whole query block (at
+  // most 256 rows); the in-sequence row offsets of all of them fit 32 bits.
+  const int64_t rows_cap = ((int64_t)max_seqlen + kMaxRowsPerBlock - 1) / kMaxRowsPerBlock *
+                           kMaxRowsPerBlock;
+  if (rows_cap * H * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
   const int waves = (dtype != FA_F32 && max_seqlen <= kVarlenNarrowMaxN) ? kWavesNarrow : kWavesPingPong;
   const int br = dtype == FA_F32 ? fa::kRowsPerBlockF32 : 32 * waves;
   // Longest-first order (nseq <= 64): one workgroup per unit, at most

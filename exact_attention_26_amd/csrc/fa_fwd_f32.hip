@@ -24,6 +24,21 @@ constexpr int kThreads = 256;
 constexpr int BR = kRowsPerBlockF32;
 constexpr int BC = 32;
 
+// Combine a lane's value with that of lane l ^ 32. v_permlane32_swap
+// exchanges the two half-waves in one VALU instruction (no LDS crossbar);
+// of its two results one is the lane's own value and the other its
+// partner's, in an order that depends on the half, so both are combined.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 template <int D, bool VARLEN>
 __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(FwdParams p) {
   constexpr int KSTR = D + 1;
@@ -53,7 +68,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(FwdParams p) {
   const int qrow = u.q0 + wave * 32 + l32;
   float qf[D / 2];
 #pragma unroll
-  for (int s = 0; s < D / 2; ++s) qf[s] = (qrow < n) ? Qg[qrow * rs + 2 * s + g] : 0.f;
+  for (int s = 0; s < D / 2; ++s) qf[s] = (qrow < n) ? Qg[(int64_t)qrow * rs + 2 * s + g] : 0.f;
 
   constexpr int CPR = D / 4;               // 16-byte chunks per row
   constexpr int NCH = BC * CPR / kThreads;  // chunks per thread per tensor
@@ -67,8 +82,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(FwdParams p) {
       const int col = (c % CPR) * 4;
       f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
       if (key < n) {
-        a = *(const f32x4*)(Kg + key * rs + col);
-        b = *(const f32x4*)(Vg + key * rs + col);
+        a = *(const f32x4*)(Kg + (int64_t)key * rs + col);
+        b = *(const f32x4*)(Vg + (int64_t)key * rs + col);
       }
       kr[r] = a;
       vr[r] = b;
@@ -127,7 +142,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(FwdParams p) {
     float mx = s[0];
 #pragma unroll
     for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = halves_max(mx);
     const float mnew = fmaxf(m, mx);
     const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - mnew) * c2);
     const float mc = mnew * c2;
@@ -159,10 +174,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_f32_kernel(FwdParams p) {
     __syncthreads();
   }
 
-  l += __shfl_xor(l, 32);
+  l = halves_sum(l);
   if (qrow < n) {
     const float inv = 1.f / l;
-    float* orow = Og + qrow * rs;
+    float* orow = Og + (int64_t)qrow * rs;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll

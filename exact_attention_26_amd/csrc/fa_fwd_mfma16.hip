@@ -135,7 +135,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
 #pragma unroll
   for (int s = 0; s < D / 16; ++s) {
     u32x4 w = {0u, 0u, 0u, 0u};
-    if (qrow < n) w = *(const u32x4*)(Qg + qrow * rs + 16 * s + 8 * g);
+    if (qrow < n) w = *(const u32x4*)(Qg + (int64_t)qrow * rs + 16 * s + 8 * g);
     qf[s] = __builtin_bit_cast(vec8, w);
   }
 
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   // Write-back: divide once by l, L = m*scale + ln l.
   if (qrow < n) {
     const float inv = 1.f / l;
-    unsigned short* orow = Og + qrow * rs;
+    unsigned short* orow = Og + (int64_t)qrow * rs;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll

@@ -91,6 +91,22 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
 
 /*
  * Packed variable-length forward (self-attention within each sequence).
+ *
+ * Basis: the pages describe no variable-length forward. Their kernel runs
+ * one (batch, head) of length N per set of blocks ("Kernel visualization:
+ * Flash Attention 2", "Steps" and "Same operations in another block"), and
+ * the flash-attention documentation mentions packed variable-length batches
+ * only for the backward's dq_accum padding. This entry point is that same
+ * per-head computation applied to every sequence of a packed batch, which
+ * is this library's reading of the north-star's "varlen entry taking
+ * cumulative sequence offsets": token-major [T, H, d] tensors, one offset
+ * array shared by queries and keys, L as [H, T].
+ *
+ * total_tokens is an argument of its own because T = cu_seqlens[nseq] lives
+ * in device memory: the host needs T, without a synchronising read of the
+ * device, to bound the extents of Q, K, V, O and L for the alias and size
+ * checks and to size the launch grid.
+ *
  *   Q, K, V, O   : contiguous [T, H, d] tensors of `dtype`; token t of
  *                  head h at (t*H + h)*d. Sequence s owns tokens
  *                  cu_seqlens[s] .. cu_seqlens[s+1]-1 and attends to those
@@ -104,7 +120,9 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
  *                  the grid. Of a longer sequence, the first max_seqlen rows
  *                  are computed (against all of its keys), and the rows past
  *                  max_seqlen rounded up to the kernel's query block (128 or
- *                  256 rows) are not written. max_seqlen*H*d must be below 2^31.
+ *                  256 rows) are not written. max_seqlen rounded up to a
+                  multiple of 256, times H*d, must be below 2^31
+                  (FA_ERR_SIZE otherwise).
  * Returns an fa_status.
  */
 int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L,

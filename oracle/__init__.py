@@ -6,14 +6,17 @@ with it; the two meet only in the seeded inputs of ``workloads``.
 """
 from .attention_f64 import (  # noqa: F401
     softmax,
-    online_softmax,
+    streamed_softmax,
+    block_states,
+    merge_states,
+    reduce_states,
     attention_naive,
     attention_naive_rows,
     attention_dense,
     attention_dense_rows,
     attention_varlen,
     attention_varlen_rows,
-    attention_tiled,
+    blocked_attention,
     scores_to_weights,
 )
 from .attention_bwd_f64 import (  # noqa: F401

@@ -34,11 +34,12 @@ Every row uses ALL keys; rows may be processed in chunks because rows are
 independent ([KV] "Same operations in another block"), columns may not
 (that would be the online method under test).
 
-``attention_tiled`` is a second, independent float64 rendering of the
-tiled online algorithm of [FS] STAGE 4 (plus the scale and L of [KV]); it
-exists so the pins can check the oracle against the pages' own
-equivalence claim, and so a planted mistake (no rescale) can be shown to
-fail. It is not used to judge the GPU path.
+``blocked_attention`` is a second, independent float64 route to the same
+result: per-key-block softmax summaries combined exactly by the rescale
+rule of [FS] STAGE 3-4 and [KV]'s online update. It exists so the pins can
+check the oracle against the pages' own equivalence claim, and so a planted
+mistake (summaries combined without the rescale) can be shown to fail. It
+is not used to judge the GPU path.
 
 Parity pins for every function here live in ``tests/test_oracle.py``
 (brute force at 50 digits, a library attention routine, scipy's
@@ -84,20 +85,84 @@ def scores_to_weights(S):
 
 
 # ---------------------------------------------------------------------------
-# [FS] STAGE 3: online softmax over one row seen a block at a time.
-# The running max m and running sum l are carried; when a block raises the
-# max, the old sum is brought to the new baseline by exp(m_old - m_new).
+# Partial softmax states ([FS] STAGE 3; [KV] "Iteration j = 0/1").
+#
+# The scores of a set of keys, seen against a reference value r, are
+# summarised by the triple (r, mass, wsum): mass = sum_c exp(x_c - r) and,
+# when values come along, wsum = sum_c exp(x_c - r) v_c. Summaries of two
+# disjoint key sets combine exactly once both are expressed against a common
+# reference; the larger of the two keeps every exponent <= 0. Re-expressing
+# a summary against a new reference multiplies mass and wsum by
+# exp(r_old - r_new) -- the rescale step the pages apply whenever the
+# running max moves. A summary of no keys has r = -inf and contributes
+# nothing (factor 0).
+#
+# The functions below cut the keys into blocks, summarise every block
+# against its own maximum (vectorised), and combine the summaries with a
+# balanced pairwise reduction. `align=False` drops the re-expression (the
+# pages' planted bug: masses taken against different references are added
+# as if they shared one); `align_values=False` re-expresses mass but not
+# wsum. Both must fail the equivalence pins.
 # ---------------------------------------------------------------------------
-def online_softmax(row, block: int = 8, rescale: bool = True) -> np.ndarray:
+def _to_common(ref_a, ref_b):
+    """Factors that bring summaries at references ref_a and ref_b to
+    max(ref_a, ref_b); an empty summary (reference -inf) gets factor 0."""
+    top = np.maximum(ref_a, ref_b)
+    with np.errstate(invalid="ignore"):
+        fa = np.where(np.isneginf(ref_a), 0.0, np.exp(ref_a - top))
+        fb = np.where(np.isneginf(ref_b), 0.0, np.exp(ref_b - top))
+    return top, fa, fb
+
+
+def merge_states(a, b, align: bool = True, align_values: bool = True):
+    """Combine two summaries (ref, mass, wsum) of disjoint key sets. ref and
+    mass have one entry per query row; wsum has one row of values per query
+    row, or is None."""
+    ra, ma, wa = a
+    rb, mb, wb = b
+    top, fa, fb = _to_common(ra, rb)
+    if not align:
+        fa, fb = np.ones_like(fa), np.ones_like(fb)
+    mass = fa * ma + fb * mb
+    if wa is None:
+        return top, mass, None
+    ga, gb = (fa, fb) if align_values else (np.ones_like(fa), np.ones_like(fb))
+    return top, mass, ga[:, None] * wa + gb[:, None] * wb
+
+
+def block_states(scores, values=None, width: int = 64):
+    """Summaries of consecutive key blocks of `width` columns of a score
+    matrix (rows = queries), each against its own block maximum."""
+    x = np.atleast_2d(_f64(scores))
+    out = []
+    for c0 in range(0, x.shape[1], width):
+        blk = x[:, c0:c0 + width]
+        ref = blk.max(axis=1)
+        with np.errstate(invalid="ignore"):
+            e = np.where(np.isneginf(ref)[:, None], 0.0, np.exp(blk - ref[:, None]))
+        wsum = None if values is None else e @ values[c0:c0 + width]
+        out.append((ref, e.sum(axis=1), wsum))
+    return out
+
+
+def reduce_states(states, align: bool = True, align_values: bool = True):
+    """Combine a list of summaries by a balanced pairwise reduction."""
+    states = list(states)
+    while len(states) > 1:
+        nxt = [merge_states(states[i], states[i + 1], align, align_values)
+               for i in range(0, len(states) - 1, 2)]
+        if len(states) % 2:
+            nxt.append(states[-1])
+        states = nxt
+    return states[0]
+
+
+def streamed_softmax(row, width: int = 8, align: bool = True) -> np.ndarray:
+    """Softmax of one row from blockwise summaries: the row's weights are
+    exp(x - ref) / mass of the combined summary."""
     x = _f64(row).reshape(-1)
-    ref, total = -np.inf, 0.0          # running max, sum of exp(x - ref)
-    for b in range(0, x.size, block):
-        part = x[b:b + block]
-        top = max(ref, float(part.max()))
-        carry = float(np.exp(ref - top)) if (rescale and np.isfinite(ref)) else 1.0
-        total = total * carry + float(np.exp(part - top).sum())
-        ref = top
-    return np.exp(x - ref) / total
+    ref, mass, _ = reduce_states(block_states(x[None, :], None, width), align)
+    return np.exp(x - ref[0]) / mass[0]
 
 
 # ---------------------------------------------------------------------------
@@ -177,50 +242,25 @@ def attention_varlen_rows(q, k, v, cu_seqlens, scale: float, seq: int, h: int, r
 
 
 # ---------------------------------------------------------------------------
-# O2: the tiled online algorithm, [FS] STAGE 4 with [KV]'s scale and L.
-#
-# The query rows are cut into blocks of Br and the keys into blocks of Bc;
-# query blocks are the outer loop. For every query row of a block three
-# running quantities are kept while the key blocks go by: the largest scaled
-# score seen so far (run_max), the sum of exp(score - run_max) (run_sum) and
-# the matching unnormalised weighted sum of value rows (acc). A key block
-# with a larger score moves run_max; the old run_sum and acc were formed
-# against the old maximum, so both are first multiplied by
-# exp(old_max - new_max) (0 for a row that has not seen any key). After the
-# last key block the row is divided by run_sum once, and its logsumexp is
-# run_max + ln(run_sum).
-#
-# `rescale=False` is [FS]'s planted bug (sums taken against different
-# baselines); `rescale_o=False` corrects run_sum but not acc. Both must fail
-# the equivalence pins.
+# O2: blocked attention from partial states ([FS] STAGE 4 with [KV]'s scale
+# and L). Query rows are cut into blocks of q_width and keys into blocks of
+# k_width; every (query block, key block) pair yields a summary of that key
+# block for those rows, the summaries of a query block are combined, and
+# the row is normalised once at the end: O = wsum / mass and
+# L = ref + ln(mass). The pages reach the same result by carrying the
+# summary through the key blocks one at a time; combining them in a tree is
+# equally exact, and shares no structure with the GPU kernel.
 # ---------------------------------------------------------------------------
-def attention_tiled(Q, K, V, scale: float, Br: int = 64, Bc: int = 64,
-                    rescale: bool = True, rescale_o: bool = True):
+def blocked_attention(Q, K, V, scale: float, q_width: int = 64, k_width: int = 64,
+                      align: bool = True, align_values: bool = True):
     Q, K, V = _f64(Q), _f64(K), _f64(V)
-    n_q, n_k = Q.shape[0], K.shape[0]
+    n_q = Q.shape[0]
     out = np.empty((n_q, V.shape[1]), dtype=np.float64)
     lse = np.empty((n_q,), dtype=np.float64)
-    key_blocks = [(a, min(a + Bc, n_k)) for a in range(0, n_k, Bc)]
-    for r0 in range(0, n_q, Br):
-        r1 = min(r0 + Br, n_q)
-        q_blk = Q[r0:r1]
-        run_max = np.full(r1 - r0, -np.inf)
-        run_sum = np.zeros(r1 - r0)
-        acc = np.zeros((r1 - r0, V.shape[1]))
-        for (c0, c1) in key_blocks:
-            scores = scale * (q_blk @ K[c0:c1].T)          # (rows, keys) block
-            new_max = np.maximum(run_max, scores.max(axis=1))
-            w = np.exp(scores - new_max[:, None])           # unnormalised weights
-            if rescale:
-                fix = np.zeros_like(run_max)
-                seen = np.isfinite(run_max)
-                fix[seen] = np.exp(run_max[seen] - new_max[seen])
-                run_sum = fix * run_sum + w.sum(axis=1)
-                acc = (fix[:, None] * acc if rescale_o else acc) + w @ V[c0:c1]
-            else:
-                run_sum = run_sum + w.sum(axis=1)
-                acc = acc + w @ V[c0:c1]
-            run_max = new_max
-        out[r0:r1] = acc / run_sum[:, None]
-        lse[r0:r1] = run_max + np.log(run_sum)
+    for r0 in range(0, n_q, q_width):
+        rows = slice(r0, min(r0 + q_width, n_q))
+        S = scale * (Q[rows] @ K.T)
+        ref, mass, wsum = reduce_states(block_states(S, V, k_width), align, align_values)
+        out[rows] = wsum / mass[:, None]
+        lse[rows] = ref + np.log(mass)
     return out, lse

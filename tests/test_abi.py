@@ -106,6 +106,10 @@ def test_dense_inputs_may_alias_each_other(lib):
     (dict(cu=0x60000002), -5), (dict(V=C + 4), -5),
     (dict(O=C), -6), (dict(L=0x60000000 - 16), -6),
     (dict(maxlen=1 << 20, T=1 << 20, H=16, d=128), -9),
+    # max_seqlen * H * d fits 2^31, but not once rounded up to a 256-row
+    # query block: the rows of that last block would overflow 32 bits.
+    (dict(maxlen=(1 << 20) - 1, T=1 << 20, H=16, d=128), -9),
+    (dict(maxlen=(1 << 20) - 256, T=1 << 20, H=16, d=128), -6),
 ])
 def test_varlen_validation(lib, kw, status):
     assert varlen(lib, **kw) == status

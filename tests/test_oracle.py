@@ -199,8 +199,8 @@ def test_online_softmax_demo():
     # [FS] DEMO 2: 32 scores ~ N(0, 3) streamed in 4 blocks of 8.
     row = np.random.default_rng(1).normal(0, 3, 32)
     ref = scipy.special.softmax(row)
-    good = oracle.online_softmax(row, block=8, rescale=True)
-    bad = oracle.online_softmax(row, block=8, rescale=False)
+    good = oracle.streamed_softmax(row, width=8, align=True)
+    bad = oracle.streamed_softmax(row, width=8, align=False)
     assert np.max(np.abs(good - ref)) <= 1e-15
     assert np.max(np.abs(oracle.softmax(row) - ref)) <= 1e-15
     assert abs(bad.sum() - 1.0) > 1e-3          # the page: "not 1.0"
@@ -223,7 +223,7 @@ def test_exactness_demo():
     # keys is a different function and must not agree.
     Q, K, V = _unit_scaled_inputs(512, 64, 5)
     ref, _ = oracle.attention_naive(Q, K, V, 1.0)
-    flash, _ = oracle.attention_tiled(Q, K, V, 1.0, Br=64, Bc=64)
+    flash, _ = oracle.blocked_attention(Q, K, V, 1.0, q_width=64, k_width=64)
     assert np.allclose(ref, flash, atol=1e-10)
     pos = np.arange(512)
     window = np.abs(pos[:, None] - pos[None, :]) <= 64
@@ -244,7 +244,7 @@ def test_tiled_equals_definition(Br, Bc):
     K = 2 * rng.standard_normal((m, d))
     V = rng.standard_normal((m, d))
     O1, L1 = oracle.attention_naive(Q, K, V, 0.5)
-    O2, L2 = oracle.attention_tiled(Q, K, V, 0.5, Br=Br, Bc=Bc)
+    O2, L2 = oracle.blocked_attention(Q, K, V, 0.5, q_width=Br, k_width=Bc)
     assert np.max(np.abs(O1 - O2)) <= 1e-12
     assert np.max(np.abs(L1 - L2)) <= 1e-12
 
@@ -259,11 +259,11 @@ def _ascending_problem():
     return Q, K, V
 
 
-@pytest.mark.parametrize("mutation", [dict(rescale=False), dict(rescale_o=False)])
+@pytest.mark.parametrize("mutation", [dict(align=False), dict(align_values=False)])
 def test_mutation_teeth(mutation):
     Q, K, V = _ascending_problem()
     O1, L1 = oracle.attention_naive(Q, K, V, 1.0)
-    O2, L2 = oracle.attention_tiled(Q, K, V, 1.0, Br=4, Bc=8, **mutation)
+    O2, L2 = oracle.blocked_attention(Q, K, V, 1.0, q_width=4, k_width=8, **mutation)
     assert np.max(np.abs(O1 - O2)) > 1e-3 or np.max(np.abs(L1 - L2)) > 1e-3
 
 
@@ -321,3 +321,40 @@ def test_torch_inputs_accepted():
     O, L = oracle.attention_naive(q, k, v, 0.125)
     Ob, Lb = brute_force(q.double().numpy(), k.double().numpy(), v.double().numpy(), 0.125)
     assert np.max(np.abs(O - Ob)) <= 1e-13 and np.max(np.abs(L - Lb)) <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# The partial-state combine behind blocked_attention: exact for any split of
+# the keys and any combination order, and an empty summary is neutral.
+# ---------------------------------------------------------------------------
+def test_merge_states_matches_logsumexp_of_union():
+    rng = np.random.default_rng(21)
+    x = 5 * rng.standard_normal((3, 40))
+    v = rng.standard_normal((40, 6))
+    for cut in (1, 13, 39):
+        a = oracle.block_states(x[:, :cut], v[:cut], width=cut)[0]
+        b = oracle.block_states(x[:, cut:], v[cut:], width=40)[0]
+        for first, second in ((a, b), (b, a)):
+            ref, mass, wsum = oracle.merge_states(first, second)
+            assert np.max(np.abs(ref + np.log(mass) - scipy.special.logsumexp(x, axis=1))) <= 1e-13
+            assert np.max(np.abs(wsum / mass[:, None] - scipy.special.softmax(x, axis=1) @ v)) <= 1e-13
+
+
+def test_merge_states_empty_summary_is_neutral():
+    rng = np.random.default_rng(22)
+    x = rng.standard_normal((2, 9))
+    v = rng.standard_normal((9, 3))
+    s = oracle.block_states(x, v, width=9)[0]
+    empty = (np.full(2, -np.inf), np.zeros(2), np.zeros((2, 3)))
+    for got in (oracle.merge_states(s, empty), oracle.merge_states(empty, s)):
+        assert np.array_equal(got[0], s[0])
+        assert np.max(np.abs(got[1] - s[1])) == 0.0
+        assert np.max(np.abs(got[2] - s[2])) == 0.0
+
+
+@pytest.mark.parametrize("width", [1, 2, 3, 5, 8, 31])
+def test_reduce_states_any_width(width):
+    rng = np.random.default_rng(width)
+    row = 4 * rng.standard_normal(31)
+    assert np.max(np.abs(oracle.streamed_softmax(row, width=width) -
+                         scipy.special.softmax(row))) <= 1e-15
