@@ -61,6 +61,7 @@
 #ifndef FA_RESCALE_TAU
 #define FA_RESCALE_TAU 8
 #endif
+static_assert(FA_RESCALE_TAU >= 5 && FA_RESCALE_TAU <= 15, "a lane sums 2^5 values of p; p must fit fp16");
 #ifndef FA_PP_PRIO
 #define FA_PP_PRIO 1
 #endif
@@ -326,17 +327,46 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   float m = BAND ? -1e30f : -INFINITY;
   f32x16 sc[2];         // scores of the next tile
 
-  // Softmax half for the score tile in sc (keys kb..kb+63), without a row
-  // max in the common case: p = exp2(s*c - m*c) against the current
-  // reference m, summed per lane. p >= 0, so a lane sum <= 2^FA_RESCALE_TAU
-  // bounds every p of that lane; when that holds in every lane, m stays.
-  // Otherwise (a score came near or above the bound; rare once m has
-  // settled) the row max is taken, O and l are rescaled to it exactly by
-  // alpha = exp2((m_old - m_new)*c), and p is recomputed from the scores,
-  // which are still in sc. On the first tile m = -inf, every lane sum is
-  // +inf (or NaN next to a masked key) and this exact path runs with
-  // alpha = 0. Then row sums, and P rounded and packed for P.V.
-  auto softmax = [&](bool ragged, int kb) __attribute__((always_inline)) {
+  // Softmax half for the score tile in sc (keys kb..kb+63). Every form keeps
+  // each p = exp2(s*c - m*c) at most 2^FA_RESCALE_TAU:
+  //  * kSpeculative: no row max. p is formed against the current reference
+  //    m and summed per lane; p >= 0, so a lane sum <= 2^FA_RESCALE_TAU
+  //    bounds every p of that lane, and when that holds in every lane m
+  //    stays. Otherwise (a score came near or above the bound; rare once m
+  //    has settled) the row max is taken, O and l are rescaled to it exactly
+  //    by alpha = exp2((m_old - m_new)*c), and p is recomputed from the
+  //    scores, which are still in sc.
+  //  * kMaxFirst (the first tile, where m is still the initial value): the
+  //    row max is taken first and becomes m; p is computed once. O and l are
+  //    still zero, so nothing is rescaled.
+  //  * kAdaptive: kSpeculative while the max has settled; after a tile that
+  //    needed the exact path, the speculative pass is skipped and the row
+  //    max is taken first (m stays if no lane's max exceeds it by more than
+  //    (TAU-5)/c, so that a lane's 32 p sum to at most 2^TAU; otherwise O
+  //    and l are rescaled to the new max first) until a tile needs no
+  //    rescale. Inputs whose max keeps moving (large logits) then pay one
+  //    exponential per score instead of two. Used at d = 64, where the
+  //    softmax is the larger share of a step (measured back to back: 13-15 %
+  //    faster on large-logit inputs at N = 512, 1.5 % on N(0,1) inputs at
+  //    N = 1024, no change at N = 2048). At d = 128 it cost 0.75 % on packed
+  //    batches and gained nothing on long sequences, where the max settles
+  //    within a few of 32 or more tiles; d = 128 keeps kSpeculative.
+  // Then row sums, and P rounded and packed for P.V.
+  enum { kSpeculative, kMaxFirst, kAdaptive };
+  // kAdaptive: wave-uniform, the last tile needed no rescale (the first tile,
+  // kMaxFirst, leaves m at its exact row max).
+  bool settled = true;
+  auto rescale_to = [&](float mnew) __attribute__((always_inline)) {
+    const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c2);
+#pragma unroll
+    for (int t = 0; t < D / 32; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
+    l *= alpha;
+    m = mnew;
+  };
+  auto softmax = [&](auto form, bool ragged, int kb) __attribute__((always_inline)) {
+    constexpr int FORM = decltype(form)::value;
     if (ragged || band_edge(kb)) mask(sc, kb);
     f32x16 pf[2];
     // Three groups fenced apart: the 32 exponent arguments, the 32
@@ -364,19 +394,38 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
           ls[i & 3] = (kt == 0 && i < 4) ? pf[kt][i] : ls[i & 3] + pf[kt][i];
       return (ls[0] + ls[1]) + (ls[2] + ls[3]);
     };
-    float lsum = exps();
-    if (__any(!(lsum <= (float)(1u << FA_RESCALE_TAU)))) {
-      const float mx = rowmax(sc);
-      if (__any(mx > m)) {
-        const float mnew = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c2);
-#pragma unroll
-        for (int t = 0; t < D / 32; ++t)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o[t][i] *= alpha;
-        l *= alpha;
-        m = mnew;
+    float lsum;
+    if constexpr (FORM == kMaxFirst) {
+      m = fmaxf(m, rowmax(sc));  // a band's fully masked lane keeps its -1e30
+      lsum = exps();
+    } else if constexpr (FORM == kAdaptive) {
+      // The speculative pass runs only while the max has settled; otherwise
+      // (or when it fails) the exact path runs: the row max, a rescale if
+      // some lane's max exceeds m by more than (TAU-5)/c (after a failed
+      // speculative pass one always does: a lane sum above 2^TAU needs a p
+      // above 2^(TAU-5)), and the exponentials against the final m. One
+      // rescale site: with two, the compiler copied all of O every tile.
+      bool exact = true;
+      if (settled) {
         lsum = exps();
+        exact = __any(!(lsum <= (float)(1u << FA_RESCALE_TAU)));
+      }
+      if (exact) {
+        const float mx = rowmax(sc);
+        // (mx - m)*c is -inf for a lane whose keys here are all masked
+        // (band), so only moved maxima count.
+        settled = !__any((mx - m) * c2 > (float)(FA_RESCALE_TAU - 5));
+        if (!settled) rescale_to(fmaxf(m, mx));
+        lsum = exps();
+      }
+    } else {
+      lsum = exps();
+      if (__any(!(lsum <= (float)(1u << FA_RESCALE_TAU)))) {
+        const float mx = rowmax(sc);
+        if (__any(mx > m)) {
+          rescale_to(fmaxf(m, mx));
+          lsum = exps();
+        }
       }
     }
     l += lsum;
@@ -391,6 +440,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
     }
     __asm__ volatile("" : "+v"(l));
   };
+  using LoopForm = std::integral_constant<int, D == 64 ? kAdaptive : kSpeculative>;
   // Operand registers of the matrix half. Reads run FA_PP_AHEAD MFMA steps
   // ahead of their MFMAs in rotating registers; the first FA_PP_AHEAD reads
   // of a matrix half are issued early, in the wave's preceding softmax half,
@@ -468,7 +518,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
     if constexpr (decltype(has_next)::value) {
       preread(KN::value, VN::value);
       if (!grp_a) copies(KS{}, VS{}, t);
-      softmax(t + 1 == rag, (t0 + t + 1) * BC);
+      softmax(LoopForm{}, t + 1 == rag, (t0 + t + 1) * BC);
     }
     __syncthreads();
   };
@@ -513,7 +563,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   // 7.2) miscompiled a three-way branch with a constant-stage read in each
   // arm (the ph == 2 arm read K through an address register it never set).
   preread(stage_of(1), stage_of(0));
-  softmax(rag == 0, t0 * BC);
+  softmax(std::integral_constant<int, kMaxFirst>{}, rag == 0, t0 * BC);
   __syncthreads();  // the K stage of tile 0 is free for tile S
   if (!grp_a) {
     if (S < tiles) fetch_k(stage_of(S), (t0 + S) * BC, rag == S);

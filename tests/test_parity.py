@@ -5,10 +5,10 @@ Bounds (max |GPU - oracle|): fp32 O <= 2e-5, L <= 1e-5; bf16/fp16
 O <= 2e-2, L <= 5e-3.
 
 Small problems are compared in full; they span several query blocks and
-key tiles and end in ragged tails. The full-size workloads are compared
-in full where the oracle finishes in seconds, otherwise on sampled rows
-(rows are independent, so each sampled row is exact against all keys),
-plus properties that hold at any size.
+key tiles and end in ragged tails. Every full-size workload is compared in
+full, every head and row (the two largest on a thread pool of oracle
+calls, about 20 s each on the host); the largest are also compared on
+sampled edge rows, and on properties that hold at any size.
 """
 import math
 
@@ -110,6 +110,62 @@ def test_workload_long_bf16_sampled():
         O_ref, L_ref = oracle.attention_dense_rows(w["q"], w["k"], w["v"], w["scale"], b, h, rows)
         assert_close(f"long_bf16 O[b={b},h={h}]", f64(o[b, h, rows]), O_ref, tol_o)
         assert_close(f"long_bf16 L[b={b},h={h}]", f64(lse[b, h, rows]), L_ref, tol_l)
+
+
+def _oracle_parallel(jobs, workers=8):
+    """Run independent oracle calls (one per head or sequence) on a thread
+    pool; numpy's BLAS and exp release the GIL. BLAS threads per call are
+    capped so the pool does not oversubscribe the host."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=2, user_api="blas"), ThreadPoolExecutor(workers) as ex:
+        return list(ex.map(lambda job: job(), jobs))
+
+
+def test_workload_long_bf16_full():
+    # Every (batch, head) of the long-sequence workload against the oracle,
+    # element by element: each block runs the same steps on its own data
+    # ("Kernel visualization: Flash Attention 2", "Same operations in another
+    # block"), so every block is checked. About 2.2 TFLOP of float64.
+    dev = device()
+    w = workloads.make("long_bf16")
+    B, H, N, d = w["B"], w["H"], w["N"], w["d"]
+    announce(f"workload long_bf16 B={B} H={H} N={N} d={d} (every head, every row)")
+    o, lse = run_dense(w["q"], w["k"], w["v"], w["scale"], dev)
+    o, lse = o.cpu(), lse.cpu()
+    q, k, v = (f64(t) for t in (w["q"], w["k"], w["v"]))
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    refs = _oracle_parallel([
+        (lambda b=b, h=h: oracle.attention_naive(q[b, h], k[b, h], v[b, h], w["scale"]))
+        for (b, h) in heads])
+    tol_o, tol_l = TOL["bf16"]
+    for (b, h), (O_ref, L_ref) in zip(heads, refs):
+        assert_close(f"long_bf16 O[b={b},h={h}]", f64(o[b, h]), O_ref, tol_o)
+        assert_close(f"long_bf16 L[b={b},h={h}]", f64(lse[b, h]), L_ref, tol_l)
+
+
+def test_workload_varlen_full():
+    # Every (sequence, head) of the packed workload, element by element.
+    dev = device()
+    w = workloads.make("varlen_bf16")
+    lengths, cu, H = w["lengths"], w["cu_seqlens"], w["H"]
+    announce(f"workload varlen_bf16 nseq={len(lengths)} T={int(cu[-1])} H={H} "
+             f"(every sequence and head, every row)")
+    o, lse = run_varlen(w["q"], w["k"], w["v"], cu, w["max_seqlen"], w["scale"], dev)
+    o, lse = o.cpu(), lse.cpu()
+    q, k, v = (f64(t) for t in (w["q"], w["k"], w["v"]))
+    jobs, keys = [], []
+    for s in range(len(lengths)):
+        a, e = int(cu[s]), int(cu[s + 1])
+        for h in range(H):
+            keys.append((s, h, a, e))
+            jobs.append(lambda a=a, e=e, h=h: oracle.attention_naive(q[a:e, h], k[a:e, h],
+                                                                      v[a:e, h], w["scale"]))
+    refs = _oracle_parallel(jobs)
+    tol_o, tol_l = TOL["bf16"]
+    for (s, h, a, e), (O_ref, L_ref) in zip(keys, refs):
+        assert_close(f"varlen O[seq={s},h={h}]", f64(o[a:e, h]), O_ref, tol_o)
+        assert_close(f"varlen L[seq={s},h={h}]", f64(lse[h, a:e]), L_ref, tol_l)
 
 
 def test_workload_varlen_sampled():

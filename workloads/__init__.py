@@ -96,6 +96,36 @@ def dense_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,
     return draw_qkv(rng, (B, H, N, d), dtype, qk_std, v_uniform)
 
 
+def moving_max_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,
+                      rate: float = 0.5, spikes: int = 0):
+    """Dense [B,H,N,d] Q, K, V (CPU tensors of `dtype`) whose scores make a
+    running row maximum move many times along the keys.
+
+    Q, K, V ~ N(0,1) as dense_inputs draws them; then every query gets a
+    first component of at least 1, and
+      spikes == 0: key c gets rate*c added to its first component, so every
+                   query's scores rise along the keys and the running max
+                   moves in nearly every key tile;
+      spikes > 0:  `spikes` keys per head, at seeded random positions, get
+                   first components 16, 32, 48, ... in key order, so the
+                   running max jumps at a few tiles and stays put between.
+    """
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, d)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    q[..., 0] = 1.0 + np.abs(q[..., 0])
+    if spikes == 0:
+        k[..., 0] += np.float32(rate) * np.arange(N, dtype=np.float32)
+    else:
+        for b in range(B):
+            for h in range(H):
+                pos = np.sort(rng.choice(N, size=min(spikes, N), replace=False))
+                k[b, h, pos, 0] = 16.0 * np.arange(1, pos.size + 1, dtype=np.float32)
+    return _round(q, dtype), _round(k, dtype), _round(v, dtype)
+
+
 def dense_bwd_inputs(B: int, H: int, N: int, d: int, dtype: str, seed: int = 0,
                      qk_std: float = 1.0, v_uniform: bool = False):
     """Q, K, V as dense_inputs draws them, then the upstream gradient dO ~ N(0,1)
