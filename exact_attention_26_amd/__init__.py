@@ -15,6 +15,8 @@ PyTorch supplies device memory and the current stream.
                     dtype, stream)                                  -> None
     fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, delta, B, H, N, d, scale,
            dtype, stream)                                           -> None
+    fa_bwd_noalloc(Q, K, V, O, dO, L, dQ, dK, dV, B, H, N, d, scale,
+                   dtype, stream)                                   -> None
     fa_dropout_add_norm(x0, x1, residual, gamma0, beta0, gamma1, beta1,
                         y0, y1, z, mean, rstd, mask, rows, hidden,
                         dropout_p, seed, offset, eps, norm, dtype,
@@ -47,6 +49,7 @@ import threading
 __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "LIB_PATH", "load", "fa_fwd", "fa_fwd_varlen",
     "fa_strerror", "fa_version", "forward", "forward_varlen", "EXPORTED_SYMBOLS", "fa_bwd",
+    "fa_bwd_noalloc",
     "backward", "fa_fwd_banded", "forward_banded", "fa_fwd_kv_outer", "forward_kv_outer",
     "fa_dropout_add_norm", "dropout_add_norm", "FA_NORM_LAYER", "FA_NORM_RMS",
 ]
@@ -56,10 +59,10 @@ FA_NORM_LAYER, FA_NORM_RMS = 0, 1
 STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_HEADDIM", -4: "FA_ERR_DTYPE",
     -5: "FA_ERR_ALIGN", -6: "FA_ERR_ALIAS", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_SCALE",
-    -9: "FA_ERR_SIZE", -10: "FA_ERR_ARG",
+    -9: "FA_ERR_SIZE", -10: "FA_ERR_ARG", -11: "FA_ERR_SCRATCH",
 }
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_banded", "fa_fwd_kv_outer", "fa_bwd",
-                    "fa_dropout_add_norm", "fa_strerror", "fa_version")
+                    "fa_bwd_noalloc", "fa_dropout_add_norm", "fa_strerror", "fa_version")
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 _lib = None
@@ -100,6 +103,8 @@ def _load_locked() -> ctypes.CDLL:
     lib.fa_dropout_add_norm.restype = i32
     lib.fa_bwd.argtypes = [vp] * 10 + [i32, i32, i32, i32, f32, i32, vp]
     lib.fa_bwd.restype = i32
+    lib.fa_bwd_noalloc.argtypes = [vp] * 9 + [i32, i32, i32, i32, f32, i32, vp]
+    lib.fa_bwd_noalloc.restype = i32
     lib.fa_strerror.argtypes = [i32]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -154,6 +159,11 @@ def fa_dropout_add_norm(x0, x1, residual, gamma0, beta0, gamma1, beta1, y0, y1, 
 def fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, delta, B, H, N, d, scale, dtype, stream) -> None:
     _check(load().fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, delta, int(B), int(H), int(N), int(d),
                          float(scale), int(dtype), stream))
+
+
+def fa_bwd_noalloc(Q, K, V, O, dO, L, dQ, dK, dV, B, H, N, d, scale, dtype, stream) -> None:
+    _check(load().fa_bwd_noalloc(Q, K, V, O, dO, L, dQ, dK, dV, int(B), int(H), int(N), int(d),
+                                 float(scale), int(dtype), stream))
 
 
 # ---------------------------------------------------------------------------

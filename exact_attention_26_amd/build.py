@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.hip", "fa_fwd_f32.hip", "fa_fwd_mfma16.hip", "fa_fwd_kvouter.hip", "fa_norm.hip",
+SOURCES = ["fa_api.hip", "fa_noalloc.hip", "fa_fwd_f32.hip", "fa_fwd_mfma16.hip", "fa_fwd_kvouter.hip",
+           "fa_norm.hip",
            "fa_bwd.hip"]
 # Per-source extra flags. The backward's key-block kernel runs one wave per
 # SIMD with >256 live registers; left to itself the compiler gives every

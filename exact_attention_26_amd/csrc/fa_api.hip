@@ -36,7 +36,7 @@ constexpr int kVarlenNarrowMaxN = FA_VARLEN_NARROW_MAX_N;  // max_seqlen
 // Largest query block of any forward kernel (the 8-wave 16-bit one).
 constexpr int kMaxRowsPerBlock = 256;
 
-constexpr int kVersion = 500;  // 0.5.0: adds fa_dropout_add_norm
+constexpr int kVersion = 600;  // 0.6.0: adds fa_bwd_noalloc
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -87,6 +87,65 @@ bool grid_fits(int64_t blocks, int threads) { return blocks <= kMaxWorkItems / t
 int fwd_threads(int dtype, int waves) { return dtype == FA_F32 ? kThreadsDefault : 64 * waves; }
 
 }  // namespace
+
+namespace fa {
+
+int prepare_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                const float* L, void* dQ, void* dK, void* dV, const float* delta,
+                bool caller_delta, int B, int H, int N, int d, float scale, int dtype,
+                BwdParams& p) {
+  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
+  if (B == 0 || H == 0 || N == 0) return kEmptyProblem;
+
+  if ((int64_t)N * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
+  const int kb = (N + kBwdKeysPerBlock - 1) / kBwdKeysPerBlock;
+  const int qb = (N + kBwdQueriesPerBlock - 1) / kBwdQueriesPerBlock;
+  if ((int64_t)kb * H * B > kMaxBlocks || (int64_t)qb * H * B > kMaxBlocks) return FA_ERR_SIZE;
+  const int64_t rows = (int64_t)B * H * N;
+  if ((rows + 15) / 16 > kMaxBlocks) return FA_ERR_SIZE;  // the D kernel: >= 16 rows per block
+  if (!caller_delta && rows > kBwdScratchRows) return FA_ERR_SCRATCH;
+  if (!Q || !K || !V || !O || !dO || !L || !dQ || !dK || !dV || (caller_delta && !delta))
+    return FA_ERR_NULL;
+  const void* all[] = {Q, K, V, O, dO, L, dQ, dK, dV, delta};
+  for (const void* ptr : all)
+    if (ptr && !aligned16(ptr)) return FA_ERR_ALIGN;  // delta is null only when unused
+  const uint64_t tb = (uint64_t)rows * d * 2, rb = (uint64_t)rows * 4;
+  const void* in[] = {Q, K, V, O, dO, L};
+  const uint64_t in_b[] = {tb, tb, tb, tb, tb, rb};
+  const void* out[] = {dQ, dK, dV, delta};
+  const uint64_t out_b[] = {tb, tb, tb, caller_delta ? rb : 0};
+  for (int i = 0; i < 4; ++i) {
+    for (int j = 0; j < 6; ++j)
+      if (overlap(out[i], out_b[i], in[j], in_b[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 4; ++j)
+      if (overlap(out[i], out_b[i], out[j], out_b[j])) return FA_ERR_ALIAS;
+  }
+
+  p.q = Q;
+  p.k = K;
+  p.v = V;
+  p.o = O;
+  p.dout = dO;
+  p.lse = L;
+  p.dq = dQ;
+  p.dk = dK;
+  p.dv = dV;
+  p.delta = const_cast<float*>(delta);
+  p.head_stride = (int64_t)N * d;
+  p.rows = rows;
+  p.BH = B * H;
+  p.N = N;
+  p.kblocks = kb;
+  p.qblocks = qb;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  return FA_OK;
+}
+
+}  // namespace fa
 
 extern "C" {
 
@@ -347,53 +406,10 @@ int fa_dropout_add_norm(const void* x0, const void* x1, const void* residual, co
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
            const float* L, void* dQ, void* dK, void* dV, float* delta, int B, int H, int N, int d,
            float scale, int dtype, void* stream) {
-  if (dtype != FA_F16 && dtype != FA_BF16) return FA_ERR_DTYPE;
-  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
-  if (d != 64 && d != 128) return FA_ERR_HEADDIM;
-  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_SCALE;
-  if (B == 0 || H == 0 || N == 0) return FA_OK;
-
-  if ((int64_t)N * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
-  const int kb = (N + fa::kBwdKeysPerBlock - 1) / fa::kBwdKeysPerBlock;
-  const int qb = (N + fa::kBwdQueriesPerBlock - 1) / fa::kBwdQueriesPerBlock;
-  if ((int64_t)kb * H * B > kMaxBlocks || (int64_t)qb * H * B > kMaxBlocks) return FA_ERR_SIZE;
-  const int64_t rows = (int64_t)B * H * N;
-  if ((rows + 15) / 16 > kMaxBlocks) return FA_ERR_SIZE;  // the D kernel: >= 16 rows per block
-  if (!Q || !K || !V || !O || !dO || !L || !dQ || !dK || !dV || !delta) return FA_ERR_NULL;
-  const void* all[] = {Q, K, V, O, dO, L, dQ, dK, dV, delta};
-  for (const void* ptr : all)
-    if (!aligned16(ptr)) return FA_ERR_ALIGN;
-  const uint64_t tb = (uint64_t)rows * d * 2, rb = (uint64_t)rows * 4;
-  const void* in[] = {Q, K, V, O, dO, L};
-  const uint64_t in_b[] = {tb, tb, tb, tb, tb, rb};
-  const void* out[] = {dQ, dK, dV, delta};
-  const uint64_t out_b[] = {tb, tb, tb, rb};
-  for (int i = 0; i < 4; ++i) {
-    for (int j = 0; j < 6; ++j)
-      if (overlap(out[i], out_b[i], in[j], in_b[j])) return FA_ERR_ALIAS;
-    for (int j = i + 1; j < 4; ++j)
-      if (overlap(out[i], out_b[i], out[j], out_b[j])) return FA_ERR_ALIAS;
-  }
-
   fa::BwdParams p{};
-  p.q = Q;
-  p.k = K;
-  p.v = V;
-  p.o = O;
-  p.dout = dO;
-  p.lse = L;
-  p.dq = dQ;
-  p.dk = dK;
-  p.dv = dV;
-  p.delta = delta;
-  p.head_stride = (int64_t)N * d;
-  p.rows = rows;
-  p.BH = B * H;
-  p.N = N;
-  p.kblocks = kb;
-  p.qblocks = qb;
-  p.scale = scale;
-  p.scale_log2 = scale * 1.4426950408889634f;
+  const int st = fa::prepare_bwd(Q, K, V, O, dO, L, dQ, dK, dV, delta, true, B, H, N, d, scale,
+                                 dtype, p);
+  if (st != FA_OK) return st == fa::kEmptyProblem ? FA_OK : st;
   const hipError_t e =
       fa::launch_bwd(p, d, dtype == FA_BF16, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -412,6 +428,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale must be finite and > 0";
     case FA_ERR_SIZE: return "FA_ERR_SIZE: problem too large for 32-bit in-head offsets or one launch grid";
     case FA_ERR_ARG: return "FA_ERR_ARG: an argument outside its documented range";
+    case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: problem larger than the library's static scratch buffer";
     default: return "unknown fa_status";
   }
 }

@@ -23,11 +23,12 @@
  *
  * Conventions shared by every entry point:
  *   - Every tensor argument (Q, K, V, O, L, cu_seqlens, dO, dQ, dK, dV,
- *     delta) is a DEVICE pointer, allocated and owned
- *     by the caller. The library allocates nothing, keeps no per-call state
- *     and never synchronises: work is enqueued on `stream` (a hipStream_t
- *     passed as void*; NULL = the default stream) and the caller
- *     synchronises. Calls on one stream run in order.
+ *     delta, acc) is a DEVICE pointer, allocated and owned by the caller.
+ *     No entry point allocates device memory or keeps per-call state, and
+ *     none synchronises: work is enqueued on `stream` (a hipStream_t passed
+ *     as void*; NULL = the default stream) and the caller synchronises.
+ *     Calls on one stream run in order. The one piece of library-owned
+ *     device memory is fa_bwd_noalloc's static scratch array (below).
  *   - Storage dtype of Q, K, V and O is `dtype` (fa_dtype). Arithmetic:
  *     products of dtype values summed in fp32; softmax statistics m, l in
  *     fp32; for fp16/bf16 the probabilities are rounded to dtype (round to
@@ -68,7 +69,8 @@ typedef enum {
   FA_ERR_LAUNCH = -7,   /* the HIP runtime refused the kernel launch         */
   FA_ERR_SCALE = -8,    /* scale not finite or not > 0                       */
   FA_ERR_SIZE = -9,     /* too large for 32-bit in-head offsets or one grid  */
-  FA_ERR_ARG = -10      /* an argument outside its documented range          */
+  FA_ERR_ARG = -10,     /* an argument outside its documented range          */
+  FA_ERR_SCRATCH = -11  /* larger than the library's static scratch buffer    */
 } fa_status;
 
 typedef enum {
@@ -121,8 +123,8 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
  *                  are computed (against all of its keys), and the rows past
  *                  max_seqlen rounded up to the kernel's query block (128 or
  *                  256 rows) are not written. max_seqlen rounded up to a
-                  multiple of 256, times H*d, must be below 2^31
-                  (FA_ERR_SIZE otherwise).
+ *                  multiple of 256, times H*d, must be below 2^31
+ *                  (FA_ERR_SIZE otherwise).
  * Returns an fa_status.
  */
 int fa_fwd_varlen(const void* Q, const void* K, const void* V, void* O, float* L,
@@ -254,6 +256,33 @@ int fa_dropout_add_norm(const void* x0, const void* x1, const void* residual,
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
            const float* L, void* dQ, void* dK, void* dV, float* delta,
            int B, int H, int N, int d, float scale, int dtype, void* stream);
+
+/*
+ * Dense backward that allocates nothing: fa_bwd without the delta argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). The same
+ * kernels compute the same dQ, dK, dV, bit for bit; D = rowsum(dO * O) goes
+ * to a static device array of the library instead of caller scratch.
+ *   - The array holds 2^22 float32 values (16 MiB): B*H*N must be at most
+ *     4,194,304 (FA_ERR_SCRATCH otherwise, before anything is enqueued).
+ *     Each GPU the library runs on holds its own copy from the first call on
+ *     that device until the process ends.
+ *   - The call makes no hipMalloc, hipFree or other allocating call. On its
+ *     first use on a device it looks up that device's copy of the array
+ *     (hipGetSymbolAddress, with that device current) and keeps the address;
+ *     a failed lookup returns FA_ERR_LAUNCH.
+ *   - `stream` must belong to the current device (FA_ERR_ARG otherwise).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in
+ *     time on one GPU (on different streams, or from different threads
+ *     without ordering) race on it and may return wrong gradients. Calls on
+ *     one stream run in order and are safe. Every D value is written before
+ *     it is read within a call, so nothing needs clearing between calls.
+ * Arguments, checks and conventions otherwise as for fa_bwd. Returns an
+ * fa_status.
+ */
+int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* L, void* dQ, void* dK, void* dV,
+                   int B, int H, int N, int d, float scale, int dtype, void* stream);
 
 /* Static, NUL-terminated description of an fa_status value. */
 const char* fa_strerror(int status);

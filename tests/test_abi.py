@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert fa.fa_version() == 500
+    assert fa.fa_version() == 600
     for code, name in fa.STATUS.items():
         assert fa.fa_strerror(code).startswith(name)
     assert fa.fa_strerror(12345) == "unknown fa_status"
@@ -153,6 +153,29 @@ def test_bwd_validation(lib, kw, status):
 @pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
 def test_bwd_empty_is_noop(lib, kw):
     assert bwd(lib, **kw) == 0
+
+
+def bwd_noalloc(lib, B=2, H=3, N=100, d=64, scale=0.125, dtype=fa.FA_BF16, **ptrs):
+    a = dict(BW, **ptrs)
+    return lib.fa_bwd_noalloc(a["Q"], a["K"], a["V"], a["O"], a["dO"], a["L"], a["dQ"], a["dK"],
+                              a["dV"], B, H, N, d, scale, dtype, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=fa.FA_F32), -4), (dict(B=-1), -2), (dict(d=80), -3), (dict(scale=0.0), -8),
+    (dict(dO=0), -1), (dict(dQ=0), -1), (dict(dK=BW["dK"] + 8), -5),
+    (dict(dQ=BW["Q"]), -6), (dict(dK=BW["dQ"]), -6),
+    # The static scratch holds 2^22 rows (B*H*N); one row more is refused
+    # before any pointer is looked at.
+    (dict(B=1, H=64, N=65537, dQ=0), -11), (dict(B=4, H=16, N=65536, dQ=0), -1),
+])
+def test_bwd_noalloc_validation(lib, kw, status):
+    assert bwd_noalloc(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
+def test_bwd_noalloc_empty_is_noop(lib, kw):
+    assert bwd_noalloc(lib, **kw) == 0
 
 
 def test_bwd_inputs_may_alias_each_other(lib):
