@@ -49,7 +49,7 @@ import threading
 __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "LIB_PATH", "load", "fa_fwd", "fa_fwd_varlen",
     "fa_strerror", "fa_version", "forward", "forward_varlen", "EXPORTED_SYMBOLS", "fa_bwd",
-    "fa_bwd_noalloc",
+    "fa_bwd_noalloc", "load_library", "POISON_LIB_PATH",
     "backward", "fa_fwd_banded", "forward_banded", "fa_fwd_kv_outer", "forward_kv_outer",
     "fa_dropout_add_norm", "dropout_add_norm", "FA_NORM_LAYER", "FA_NORM_RMS",
 ]
@@ -64,6 +64,7 @@ STATUS = {
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_banded", "fa_fwd_kv_outer", "fa_bwd",
                     "fa_bwd_noalloc", "fa_dropout_add_norm", "fa_strerror", "fa_version")
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+POISON_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_lds_poison.so")
 
 _lib = None
 _lib_lock = threading.Lock()
@@ -86,9 +87,17 @@ def load() -> ctypes.CDLL:
 
 def _load_locked() -> ctypes.CDLL:
     global _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m exact_attention_26_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    _lib = load_library(LIB_PATH)
+    return _lib
+
+
+def load_library(path: str) -> ctypes.CDLL:
+    """Load a build of the library at `path` and declare its C signatures.
+    load() uses it for libfa.so; tests use it for the debug variant
+    libfa_lds_poison.so (POISON_LIB_PATH)."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m exact_attention_26_amd.build`")
+    lib = ctypes.CDLL(path)
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, vp]
     lib.fa_fwd.restype = i32
@@ -109,7 +118,6 @@ def _load_locked() -> ctypes.CDLL:
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
     lib.fa_version.restype = i32
-    _lib = lib
     return lib
 
 

@@ -5,6 +5,11 @@
 Every translation unit is compiled with hipcc for gfx950 only, with packed
 fp32 VALU instructions disabled, then linked into a shared library next to
 this file. Object files go to ``_build/`` at the repository root.
+
+A second library, libfa_lds_poison.so, is built from the same sources with
+FA_DEBUG_POISON_LDS: before every LDS DMA copy is issued its destination is
+filled with NaN, so a read of a stage that is not ordered after the copy's
+completion shows up as NaN in the outputs. Only the tests load it.
 """
 from __future__ import annotations
 
@@ -18,6 +23,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
+POISON_LIB = os.path.join(PKG, "libfa_lds_poison.so")
+# Library variants: output path, extra compile flags, object directory.
+VARIANTS = [(LIB, [], BUILD),
+            (POISON_LIB, ["-DFA_DEBUG_POISON_LDS"], os.path.join(BUILD, "lds_poison"))]
 
 SOURCES = ["fa_api.hip", "fa_noalloc.hip", "fa_fwd_f32.hip", "fa_fwd_mfma16.hip", "fa_fwd_kvouter.hip",
            "fa_norm.hip",
@@ -52,20 +61,24 @@ def compile_flags() -> list[str]:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile all sources (in parallel) and link libfa.so. Returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+    """Compile all sources of every variant (in parallel) and link them.
+    Returns the path of the product library, libfa.so."""
     cc = hipcc()
     procs = []
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        objs.append(obj)
-        cmd = [cc, *compile_flags(), *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
-               "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
-                                            text=True)))
+    links = []
+    for lib, extra, objdir in VARIANTS:
+        os.makedirs(objdir, exist_ok=True)
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+            objs.append(obj)
+            cmd = [cc, *compile_flags(), *extra, *EXTRA_FLAGS.get(src, []), "-c",
+                   os.path.join(CSRC, src), "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE,
+                                                stderr=subprocess.STDOUT, text=True)))
+        links.append((lib, objs))
     failed = []
     for src, pr in procs:
         out, _ = pr.communicate()
@@ -78,12 +91,13 @@ def build(verbose: bool = False) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    tmp = LIB + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    for lib, objs in links:
+        tmp = lib + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, lib)
     return LIB
 
 

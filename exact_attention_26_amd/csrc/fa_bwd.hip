@@ -73,6 +73,7 @@ struct BTile {
 // Inline asm so the compiler does not make later LDS reads wait for it;
 // completion is awaited explicitly (vmcnt) before the publishing barrier.
 __device__ __forceinline__ void dma16(const void* gbase, unsigned lds_dst, unsigned voff) {
+  poison_lds_before_copy<16>(lds_dst);
   __asm__ volatile(
       "s_mov_b32 m0, %0\n\t"
       "global_load_lds_dwordx4 %1, %2"
@@ -82,6 +83,7 @@ __device__ __forceinline__ void dma16(const void* gbase, unsigned lds_dst, unsig
 }
 // 64 floats: lane i moves 4 bytes from gbase + voff to LDS M0 + 4*i.
 __device__ __forceinline__ void dma4(const void* gbase, unsigned lds_dst, unsigned voff) {
+  poison_lds_before_copy<4>(lds_dst);
   __asm__ volatile(
       "s_mov_b32 m0, %0\n\t"
       "global_load_lds_dword %1, %2"

@@ -62,6 +62,30 @@ __device__ __forceinline__ unsigned pack2(float a, float b) {
 }
 
 
+// Debug build only (compiled with FA_DEBUG_POISON_LDS): called by the lanes
+// of a wave right before they issue an LDS DMA copy to lds_addr (lane i
+// then writes BYTES bytes at lds_addr + BYTES*i). It fills exactly those
+// bytes with all-ones, a NaN in fp32, bf16 and fp16, and waits until the
+// fill has landed, so the copy's data is written after it. Any read of the
+// destination that is not ordered after the copy's completion (a missing
+// vmcnt wait or barrier) then sees NaN instead of stale data from an older
+// tile, and the NaN reaches the outputs. In the normal build it is empty.
+template <int BYTES>
+__device__ __forceinline__ void poison_lds_before_copy(unsigned lds_addr) {
+#ifdef FA_DEBUG_POISON_LDS
+  static_assert(BYTES == 16 || BYTES == 4, "dwordx4 or dword copies");
+  const unsigned a = lds_addr + BYTES * (threadIdx.x & 63);
+  if constexpr (BYTES == 16)
+    *(__attribute__((address_space(3))) u32x4*)(uintptr_t)a = u32x4{~0u, ~0u, ~0u, ~0u};
+  else
+    *(__attribute__((address_space(3))) unsigned*)(uintptr_t)a = ~0u;
+  __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#else
+  (void)lds_addr;
+#endif
+}
+
+
 // The chip has 8 XCDs, each with its own L2, and consecutive workgroup ids
 // are dealt to the XCDs round-robin. Work units that share K/V (the
 // Q-blocks of one head) get consecutive logical ids, so this mapping sends

@@ -173,6 +173,7 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   // location and wait for them before unrelated LDS reads; completion is
   // awaited explicitly (vmcnt(0)) before the barrier that publishes a tile.
   auto dma = [&](const unsigned short* Gt, unsigned dst, unsigned off) {
+    poison_lds_before_copy<16>(dst);
     __asm__ volatile(
         "s_mov_b32 m0, %0\n\t"
         "global_load_lds_dwordx4 %1, %2"

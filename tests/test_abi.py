@@ -62,7 +62,7 @@ def varlen(lib, Q=A, K=B_, V=C, O=D, L=E, cu=0x60000000, nseq=3, T=300, maxlen=2
     return lib.fa_fwd_varlen(Q, K, V, O, L, cu, nseq, T, maxlen, H, d, scale, dtype, None)
 
 
-@pytest.mark.parametrize("kw,status", [
+DENSE_VALIDATION_CASES = [
     (dict(dtype=3), -4), (dict(dtype=-1), -4),
     (dict(B=-1), -2), (dict(H=-2), -2), (dict(N=-5), -2),
     (dict(d=32), -3), (dict(d=96), -3), (dict(d=256), -3),
@@ -80,13 +80,18 @@ def varlen(lib, Q=A, K=B_, V=C, O=D, L=E, cu=0x60000000, nseq=3, T=300, maxlen=2
     # fp32: 256-thread workgroups of 128 rows.
     (dict(B=524288, H=1, N=4096, d=64, dtype=fa.FA_F32), -9),
     (dict(B=524287, H=1, N=4096, d=64, dtype=fa.FA_F32), -6),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", DENSE_VALIDATION_CASES)
 def test_dense_validation(lib, kw, status):
     assert dense(lib, **kw) == status
 
 
-@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0),
-                                dict(B=0, Q=0, K=0, V=0, O=0, L=0)])
+DENSE_EMPTY_IS_NOOP_CASES = [dict(B=0), dict(H=0), dict(N=0), dict(B=0, Q=0, K=0, V=0, O=0, L=0)]
+
+
+@pytest.mark.parametrize("kw", DENSE_EMPTY_IS_NOOP_CASES)
 def test_dense_empty_is_noop(lib, kw):
     assert dense(lib, **kw) == 0
 
@@ -99,7 +104,7 @@ def test_dense_inputs_may_alias_each_other(lib):
     assert dense(lib, Q=A, K=A, V=A, d=96) == -3
 
 
-@pytest.mark.parametrize("kw,status", [
+VARLEN_VALIDATION_CASES = [
     (dict(dtype=7), -4), (dict(nseq=-1), -2), (dict(T=-1), -2), (dict(maxlen=-1), -2),
     (dict(H=-1), -2), (dict(maxlen=301), -2), (dict(d=80), -3), (dict(scale=0.0), -8),
     (dict(cu=0), -1), (dict(Q=0), -1), (dict(L=0), -1),
@@ -110,12 +115,18 @@ def test_dense_inputs_may_alias_each_other(lib):
     # query block: the rows of that last block would overflow 32 bits.
     (dict(maxlen=(1 << 20) - 1, T=1 << 20, H=16, d=128), -9),
     (dict(maxlen=(1 << 20) - 256, T=1 << 20, H=16, d=128), -6),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", VARLEN_VALIDATION_CASES)
 def test_varlen_validation(lib, kw, status):
     assert varlen(lib, **kw) == status
 
 
-@pytest.mark.parametrize("kw", [dict(nseq=0), dict(T=0, maxlen=0), dict(maxlen=0), dict(H=0)])
+VARLEN_EMPTY_IS_NOOP_CASES = [dict(nseq=0), dict(T=0, maxlen=0), dict(maxlen=0), dict(H=0)]
+
+
+@pytest.mark.parametrize("kw", VARLEN_EMPTY_IS_NOOP_CASES)
 def test_varlen_empty_is_noop(lib, kw):
     assert varlen(lib, **kw) == 0
 
@@ -137,7 +148,7 @@ def bwd(lib, B=2, H=3, N=100, d=64, scale=0.125, dtype=fa.FA_BF16, **ptrs):
                       a["delta"], B, H, N, d, scale, dtype, None)
 
 
-@pytest.mark.parametrize("kw,status", [
+BWD_VALIDATION_CASES = [
     (dict(dtype=fa.FA_F32), -4), (dict(dtype=5), -4),
     (dict(B=-1), -2), (dict(N=-3), -2), (dict(d=80), -3), (dict(scale=0.0), -8),
     (dict(scale=float("nan")), -8), (dict(N=1 << 25, d=64), -9),
@@ -145,12 +156,18 @@ def bwd(lib, B=2, H=3, N=100, d=64, scale=0.125, dtype=fa.FA_BF16, **ptrs):
     (dict(dK=BW["dK"] + 8), -5), (dict(delta=BW["delta"] + 4), -5), (dict(O=BW["O"] + 2), -5),
     (dict(dQ=BW["Q"]), -6), (dict(dV=BW["dO"] + 64), -6), (dict(dK=BW["dQ"]), -6),
     (dict(delta=BW["L"]), -6), (dict(delta=BW["dV"] + 16), -6), (dict(dQ=BW["L"] - 32), -6),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", BWD_VALIDATION_CASES)
 def test_bwd_validation(lib, kw, status):
     assert bwd(lib, **kw) == status
 
 
-@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
+BWD_EMPTY_IS_NOOP_CASES = [dict(B=0), dict(H=0), dict(N=0)]
+
+
+@pytest.mark.parametrize("kw", BWD_EMPTY_IS_NOOP_CASES)
 def test_bwd_empty_is_noop(lib, kw):
     assert bwd(lib, **kw) == 0
 
@@ -161,19 +178,25 @@ def bwd_noalloc(lib, B=2, H=3, N=100, d=64, scale=0.125, dtype=fa.FA_BF16, **ptr
                               a["dV"], B, H, N, d, scale, dtype, None)
 
 
-@pytest.mark.parametrize("kw,status", [
+BWD_NOALLOC_VALIDATION_CASES = [
     (dict(dtype=fa.FA_F32), -4), (dict(B=-1), -2), (dict(d=80), -3), (dict(scale=0.0), -8),
     (dict(dO=0), -1), (dict(dQ=0), -1), (dict(dK=BW["dK"] + 8), -5),
     (dict(dQ=BW["Q"]), -6), (dict(dK=BW["dQ"]), -6),
     # The static scratch holds 2^22 rows (B*H*N); one row more is refused
     # before any pointer is looked at.
     (dict(B=1, H=64, N=65537, dQ=0), -11), (dict(B=4, H=16, N=65536, dQ=0), -1),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", BWD_NOALLOC_VALIDATION_CASES)
 def test_bwd_noalloc_validation(lib, kw, status):
     assert bwd_noalloc(lib, **kw) == status
 
 
-@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0)])
+BWD_NOALLOC_EMPTY_IS_NOOP_CASES = [dict(B=0), dict(H=0), dict(N=0)]
+
+
+@pytest.mark.parametrize("kw", BWD_NOALLOC_EMPTY_IS_NOOP_CASES)
 def test_bwd_noalloc_empty_is_noop(lib, kw):
     assert bwd_noalloc(lib, **kw) == 0
 
@@ -188,19 +211,25 @@ def banded(lib, Q=A, K=B_, V=C, O=D, L=E, B=2, H=3, N=100, d=64, window=16, scal
     return lib.fa_fwd_banded(Q, K, V, O, L, B, H, N, d, window, scale, dtype, None)
 
 
-@pytest.mark.parametrize("kw,status", [
+BANDED_VALIDATION_CASES = [
     (dict(dtype=fa.FA_F32), -4), (dict(dtype=3), -4),
     (dict(window=-1), -2), (dict(window=-(1 << 30)), -2), (dict(B=-1), -2), (dict(N=-2), -2),
     (dict(d=32), -3), (dict(scale=0.0), -8), (dict(scale=float("inf")), -8),
     (dict(N=1 << 25, d=64), -9),
     (dict(Q=0), -1), (dict(L=0), -1), (dict(K=B_ + 8), -5), (dict(L=E + 4), -5),
     (dict(O=A), -6), (dict(L=D + 16), -6),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", BANDED_VALIDATION_CASES)
 def test_banded_validation(lib, kw, status):
     assert banded(lib, **kw) == status
 
 
-@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=0, window=1 << 30)])
+BANDED_EMPTY_IS_NOOP_CASES = [dict(B=0), dict(H=0), dict(N=0), dict(N=0, window=1 << 30)]
+
+
+@pytest.mark.parametrize("kw", BANDED_EMPTY_IS_NOOP_CASES)
 def test_banded_empty_is_noop(lib, kw):
     assert banded(lib, **kw) == 0
 
@@ -215,7 +244,7 @@ def kv_outer(lib, B=2, H=3, N=100, d=64, groups=4, scale=0.125, dtype=fa.FA_BF16
                                groups, scale, dtype, None)
 
 
-@pytest.mark.parametrize("kw,status", [
+KV_OUTER_VALIDATION_CASES = [
     (dict(dtype=fa.FA_F32), -4), (dict(dtype=9), -4),
     (dict(groups=0), -2), (dict(groups=-3), -2), (dict(B=-1), -2), (dict(N=-1), -2),
     (dict(d=96), -3), (dict(scale=0.0), -8), (dict(N=1 << 25, d=64), -9),
@@ -223,12 +252,18 @@ def kv_outer(lib, B=2, H=3, N=100, d=64, groups=4, scale=0.125, dtype=fa.FA_BF16
     (dict(acc=KV["acc"] + 4), -5), (dict(O=KV["O"] + 8), -5),
     (dict(acc=KV["Q"]), -6), (dict(acc=KV["O"] - 64), -6), (dict(L=KV["acc"] + 16), -6),
     (dict(O=KV["V"] + 32), -6),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", KV_OUTER_VALIDATION_CASES)
 def test_kv_outer_validation(lib, kw, status):
     assert kv_outer(lib, **kw) == status
 
 
-@pytest.mark.parametrize("kw", [dict(B=0), dict(H=0), dict(N=0), dict(N=0, groups=0 + 1)])
+KV_OUTER_EMPTY_IS_NOOP_CASES = [dict(B=0), dict(H=0), dict(N=0), dict(N=0, groups=0 + 1)]
+
+
+@pytest.mark.parametrize("kw", KV_OUTER_EMPTY_IS_NOOP_CASES)
 def test_kv_outer_empty_is_noop(lib, kw):
     assert kv_outer(lib, **kw) == 0
 
@@ -247,7 +282,7 @@ def norm(lib, rows=64, hidden=1024, p=0.1, seed=1, offset=0, eps=1e-5, kind=0,
                                    None)
 
 
-@pytest.mark.parametrize("kw,status", [
+NORM_VALIDATION_CASES = [
     (dict(dtype=fa.FA_F32), -4), (dict(dtype=4), -4),
     (dict(rows=-1), -2), (dict(hidden=-8), -2), (dict(hidden=1020), -2), (dict(hidden=8200), -2),
     (dict(kind=2), -10), (dict(p=1.0), -10), (dict(p=-0.1), -10), (dict(p=float("nan")), -10),
@@ -257,12 +292,18 @@ def norm(lib, rows=64, hidden=1024, p=0.1, seed=1, offset=0, eps=1e-5, kind=0,
     (dict(x1=NM["x1"] + 8), -5), (dict(mask=NM["mask"] + 4), -5), (dict(rstd=NM["rstd"] + 2), -5),
     (dict(y0=NM["x0"]), -6), (dict(z=NM["res"] + 32), -6), (dict(mean=NM["g0"]), -6),
     (dict(rstd=NM["y1"] + 64), -6), (dict(mask=NM["z"]), -6),
-])
+]
+
+
+@pytest.mark.parametrize("kw,status", NORM_VALIDATION_CASES)
 def test_norm_validation(lib, kw, status):
     assert norm(lib, **kw) == status
 
 
-@pytest.mark.parametrize("kw", [dict(rows=0), dict(hidden=0), dict(rows=0, x0=0)])
+NORM_EMPTY_IS_NOOP_CASES = [dict(rows=0), dict(hidden=0), dict(rows=0, x0=0)]
+
+
+@pytest.mark.parametrize("kw", NORM_EMPTY_IS_NOOP_CASES)
 def test_norm_empty_is_noop(lib, kw):
     assert norm(lib, **kw) == 0
 
