@@ -609,9 +609,20 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   }
 
   // Write-back: divide once by l, L = m*scale + ln l.
-  if (qrow < n) {
+  //
+  // O goes out through LDS so that the global stores are whole 16-byte row
+  // chunks: a lane holds 4 consecutive d of its row per register block, so
+  // direct stores would be 8-byte pieces of 32 rows each. Every wave has
+  // passed the barrier after its last matrix half, so no LDS stage is read
+  // any more; each wave writes its 32 rows into a region of its own
+  // (rows padded by 16 bytes: the half-waves' 8-byte writes then hit
+  // distinct banks, and rows stay 16-byte aligned for the reads), and reads
+  // them back in the same wave, so no barrier is needed.
+  {
+    constexpr int OROWB = 2 * D + 16;  // bytes per staged row
+    static_assert(NW * 32 * OROWB <= S * T::STAGEB, "O staging fits the K/V stages");
+    lds_u8* ow = (lds_u8*)lds + wave * 32 * OROWB;
     const float inv = 1.f / l;
-    unsigned short* orow = Og + (int64_t)qrow * rs;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -619,9 +630,21 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
         u32x2 w;
         w[0] = pack2<BF16>(o[dt][4 * blk + 0] * inv, o[dt][4 * blk + 1] * inv);
         w[1] = pack2<BF16>(o[dt][4 * blk + 2] * inv, o[dt][4 * blk + 3] * inv);
-        *(u32x2*)(orow + dt * 32 + 8 * blk + 4 * g) = w;
+        *(__attribute__((address_space(3))) u32x2*)(ow + l32 * OROWB +
+                                                     2 * (dt * 32 + 8 * blk + 4 * g)) = w;
       }
-    if (g == 0) p.lse[u.lse_base + qrow] = m * p.scale + logf(l);
+    // Read back: per instruction, 64 / (D/8) rows of D/8 lanes x 16 bytes.
+    constexpr int LPR = D / 8;  // lanes per row
+    constexpr int RPI = 64 / LPR;
+    const int rsub = lane / LPR, cb = (lane % LPR) * 16;
+    const int row0 = u.q0 + wave * 32;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = i * RPI + rsub;
+      const u32x4 v = *(const __attribute__((address_space(3))) u32x4*)(ow + r * OROWB + cb);
+      if (row0 + r < n) *(u32x4*)(Og + (int64_t)(row0 + r) * rs + cb / 2) = v;
+    }
+    if (qrow < n && g == 0) p.lse[u.lse_base + qrow] = m * p.scale + logf(l);
   }
 }
 

@@ -121,3 +121,20 @@ def test_no_sampler_under_a_profiler(monkeypatch):
     monkeypatch.setattr(bench, "_sampler", None)
     bench.start_sclk_sampler()
     assert bench._sampler is None
+
+
+def test_cpu_baseline_packed_sample():
+    # The oracle leg on a tiny packed batch, with the "GPU" output taken from
+    # the oracle itself: the error is 0, the flop count is 4*d*sum(n^2) over
+    # the pairs it did, and the CPU model is reported.
+    import torch
+    import oracle
+    lengths = [3, 70, 5]
+    q, k, v, cu = workloads.varlen_inputs(lengths, 2, 64, "bf16", seed=4)
+    w = {"q": q, "k": k, "v": v, "cu_seqlens": cu, "H": 2, "d": 64, "scale": 0.125,
+         "name": "tiny_packed"}
+    O_ref, _ = oracle.attention_varlen(q, k, v, cu, 0.125)
+    out = bench.cpu_baseline(w, torch.from_numpy(O_ref), budget_s=60.0)
+    assert out["max_abs_err_O_vs_gpu"] == 0.0
+    assert out["kind"] == "oracle" and out["cores"] >= 1 and out["cpu_model"]
+    assert out["sample"].startswith("6 of 6 (sequence, head) pairs")
