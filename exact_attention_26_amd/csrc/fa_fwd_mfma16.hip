@@ -354,9 +354,11 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   //    within a few of 32 or more tiles; d = 128 keeps kSpeculative.
   // Then row sums, and P rounded and packed for P.V.
   enum { kSpeculative, kMaxFirst, kAdaptive };
-  // kAdaptive: wave-uniform, the last tile needed no rescale (the first tile,
-  // kMaxFirst, leaves m at its exact row max).
-  bool settled = true;
+  // kAdaptive: wave-uniform, the last tile needed no rescale. It starts
+  // false: the first tile's max (kMaxFirst) says little about whether the
+  // second tile will move it, and a failed speculative pass costs a whole
+  // pass of exponentials, a row max only a sixth of that.
+  bool settled = false;
   auto rescale_to = [&](float mnew) __attribute__((always_inline)) {
     const float alpha = __builtin_amdgcn_exp2f((m - mnew) * c2);
 #pragma unroll
