@@ -99,10 +99,10 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L,
  * Flash Attention 2", "Steps" and "Same operations in another block"), and
  * the flash-attention documentation mentions packed variable-length batches
  * only for the backward's dq_accum padding. This entry point is that same
- * per-head computation applied to every sequence of a packed batch, which
- * is this library's reading of the north-star's "varlen entry taking
- * cumulative sequence offsets": token-major [T, H, d] tensors, one offset
- * array shared by queries and keys, L as [H, T].
+ * per-head computation applied to every sequence of a packed batch, laid
+ * out the way packed batches commonly are: token-major [T, H, d] tensors,
+ * one array of cumulative sequence offsets shared by queries and keys, and
+ * L as [H, T].
  *
  * total_tokens is an argument of its own because T = cu_seqlens[nseq] lives
  * in device memory: the host needs T, without a synchronising read of the
