@@ -40,6 +40,7 @@
 
 #include "fa_bwd_params.h"
 #include "fa_device.h"
+#include "fa_lanes.h"
 
 namespace fa {
 namespace {
@@ -111,8 +112,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc = fmaf((float)va[i], (float)vb[i], acc);
   }
-#pragma unroll
-  for (int w = LPR / 2; w >= 1; w /= 2) acc += __shfl_xor(acc, w, LPR);
+  acc = lanes_sum<LPR>(acc);  // the LPR lanes of a row are an aligned group
   if (row < p.rows && part == 0) p.delta[row] = acc;
 }
 

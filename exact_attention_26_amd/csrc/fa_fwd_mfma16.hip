@@ -58,6 +58,9 @@
 //     fp32, bf16 or fp16).
 //   FA_PP_PRIO (1): s_setprio of a wave during its matrix half.
 //   FA_PP_AHEAD (2): MFMA steps between an LDS operand read and its use.
+//   FA_SKIP_IDLE (1): in packed batches, waves whose rows all lie past the
+//     end of their sequence skip their MFMAs and softmax (0: they compute on
+//     zero rows and discard the result).
 #ifndef FA_RESCALE_TAU
 #define FA_RESCALE_TAU 8
 #endif
@@ -67,6 +70,9 @@ static_assert(FA_RESCALE_TAU >= 5 && FA_RESCALE_TAU <= 15, "a lane sums 2^5 valu
 #endif
 #ifndef FA_PP_AHEAD
 #define FA_PP_AHEAD 2
+#endif
+#ifndef FA_SKIP_IDLE
+#define FA_SKIP_IDLE 1
 #endif
 
 namespace fa {
@@ -319,6 +325,14 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   // a SIMD thus work for different waves at the same time, which overlaps
   // far better than MFMAs and exponentials issued by one wave.
   const bool grp_a = NW == 8 && wave < 4;  // with NW = 4 every wave is in group B
+  // Packed batches: a wave whose 32 query rows all lie past the end of its
+  // sequence (in the ragged last block of a sequence) computes nothing; it
+  // only issues its share of the copies and takes every barrier, and its
+  // SIMD serves the other workgroup's wave there. Wave-uniform. Measured
+  // back to back: +0.1-1.2 % on packed batches; the dense instances keep
+  // the unconditional code (the branch cost a d = 64 dense shape 4.8 %
+  // through register allocation).
+  const bool busy = !(VARLEN && FA_SKIP_IDLE) || row0 < n;
   vec8 pb[4];           // P of the current tile, storage dtype: P.V B operands
   // Running max of raw q.k (scale > 0). With a band it starts at a large
   // finite negative value instead of -inf: a row may meet whole tiles with
@@ -515,13 +529,13 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
     using VS = std::integral_constant<int, F>;
     using KN = std::integral_constant<int, (F + 2) % S>;
     using VN = std::integral_constant<int, (F + 1) % S>;
-    matrix(has_next, KS{}, VS{});
+    if (busy) matrix(has_next, KS{}, VS{});
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if constexpr (decltype(has_next)::value) {
-      preread(KN::value, VN::value);
+      if (busy) preread(KN::value, VN::value);
       if (!grp_a) copies(KS{}, VS{}, t);
-      softmax(LoopForm{}, t + 1 == rag, (t0 + t + 1) * BC);
+      if (busy) softmax(LoopForm{}, t + 1 == rag, (t0 + t + 1) * BC);
     }
     __syncthreads();
   };
@@ -559,14 +573,16 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   for (int s = 0; s < D / 16; ++s) __asm__ volatile("" : : "v"(qf[s]));
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  qk(stage_of(0), sc);
   // The K stage of tile 1 is read even when there is no tile 1: the
   // registers then go unused (matrix half 0 computes no S^T). The stage
   // offsets are computed here, not chosen by a branch on ph: hipcc (ROCm
   // 7.2) miscompiled a three-way branch with a constant-stage read in each
   // arm (the ph == 2 arm read K through an address register it never set).
-  preread(stage_of(1), stage_of(0));
-  softmax(std::integral_constant<int, kMaxFirst>{}, rag == 0, t0 * BC);
+  if (busy) {
+    qk(stage_of(0), sc);
+    preread(stage_of(1), stage_of(0));
+    softmax(std::integral_constant<int, kMaxFirst>{}, rag == 0, t0 * BC);
+  }
   __syncthreads();  // the K stage of tile 0 is free for tile S
   if (!grp_a) {
     if (S < tiles) fetch_k(stage_of(S), (t0 + S) * BC, rag == S);
@@ -639,7 +655,6 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
     constexpr int LPR = D / 8;  // lanes per row
     constexpr int RPI = 64 / LPR;
     const int rsub = lane / LPR, cb = (lane % LPR) * 16;
-    const int row0 = u.q0 + wave * 32;
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
       const int r = i * RPI + rsub;

@@ -25,6 +25,7 @@
 // of the W partial sums through LDS. Mean and variance are two passes over
 // the registers (no cancellation from E[z^2] - E[z]^2).
 #include "fa_device.h"
+#include "fa_lanes.h"
 #include "fa_norm_params.h"
 
 // Build option FA_NORM_NT (1): row loads and stores are non-temporal (every
@@ -99,11 +100,7 @@ __device__ __forceinline__ u32x4 pack8(const float (&f)[8]) {
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
+__device__ __forceinline__ float wave_sum(float v) { return lanes_sum<64>(v); }
 
 // Keep bits of the 8 elements starting at flat index e0 (a multiple of 8)
 // of branch `stream`, as one bit per element in bits 0..7.
