@@ -159,9 +159,15 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B
 
   if ((int64_t)N * d >= (int64_t{1} << 31)) return FA_ERR_SIZE;
   const int waves = (dtype != FA_F32 && N <= kDenseNarrowMaxN) ? kWavesNarrow : kWavesPingPong;
-  const int br = dtype == FA_F32 ? fa::kRowsPerBlockF32 : 32 * waves;
-  if (!grid_fits((int64_t)((N + br - 1) / br) * H * B, fwd_threads(dtype, waves)))
-    return FA_ERR_SIZE;
+  // fp32 problems too small to give every CU a 128-row workgroup run the
+  // key-split form: 32-row workgroups whose waves share the keys.
+  const bool split = dtype == FA_F32 && (int64_t)((N + fa::kRowsPerBlockF32 - 1) /
+                                                   fa::kRowsPerBlockF32) * H * B <
+                                            fa::kF32SplitBelowBlocks;
+  const int br = dtype == FA_F32 ? (split ? fa::kRowsPerBlockF32Split : fa::kRowsPerBlockF32)
+                                 : 32 * waves;
+  const int threads = split ? 64 * fa::f32_key_split(d) : fwd_threads(dtype, waves);
+  if (!grid_fits((int64_t)((N + br - 1) / br) * H * B, threads)) return FA_ERR_SIZE;
   const uint64_t elems = (uint64_t)B * H * N * d;
   const int st = check_buffers(Q, K, V, O, L, elems * elem_bytes(dtype), (uint64_t)B * H * N * 4);
   if (st != FA_OK) return st;
@@ -184,6 +190,7 @@ int fa_fwd(const void* Q, const void* K, const void* V, void* O, float* L, int B
   p.scale = scale;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.window = -1;
+  p.key_split = split ? fa::f32_key_split(d) : 0;
   return launch(p, d, dtype, false, stream, waves);
 }
 

@@ -37,6 +37,9 @@ struct FwdParams {
   int units_per_head;         // varlen: > 0 runs each head's units longest sequence
                               // first, this many workgroups per head (at least the
                               // head's units); 0 = one workgroup per (block, seq, head)
+  int key_split;              // fp32 dense only: > 0 runs the key-split kernel, this many
+                              // waves sharing each 32-row block (q_blocks counts 32-row
+                              // blocks); 0 = the 128-row kernel
 };
 
 // Packed batches of at most this many sequences take the longest-first order.
@@ -55,7 +58,14 @@ hipError_t launch_fwd_f32(const FwdParams& p, int d, bool varlen, hipStream_t st
 hipError_t launch_fwd_mfma16(const FwdParams& p, int d, bool bf16, bool varlen, int waves,
                              hipStream_t stream);
 
-// Query rows per workgroup of the fp32 kernel (sizes its grid).
+// Query rows per workgroup of the fp32 kernel (sizes its grid), and of its
+// key-split form, which runs when the 128-row grid would hold fewer
+// workgroups than the chip has CUs.
 constexpr int kRowsPerBlockF32 = 128;
+constexpr int kRowsPerBlockF32Split = 32;
+constexpr int kF32SplitBelowBlocks = 256;
+// Waves per 32-row block of the key-split form (its LDS holds one K/V tile
+// per wave).
+constexpr int f32_key_split(int d) { return d == 64 ? 8 : 4; }
 
 }  // namespace fa

@@ -44,14 +44,18 @@ void check_fwd(const fa::FwdParams& p, int rows_per_block) {
 
 namespace fa {
 
-hipError_t launch_fwd_f32(const FwdParams& p, int d, bool, hipStream_t) {
+hipError_t launch_fwd_f32(const FwdParams& p, int d, bool varlen, hipStream_t) {
   expect(d == 64 || d == 128, "head dim");
-  check_fwd(p, kRowsPerBlockF32);
+  expect(p.key_split == 0 || (!varlen && p.key_split == f32_key_split(d)), "key split");
+  expect(p.key_split == 0 || (int64_t)((p.N + kRowsPerBlockF32 - 1) / kRowsPerBlockF32) * p.H *
+                                     p.B < kF32SplitBelowBlocks, "key split on a large grid");
+  check_fwd(p, p.key_split ? kRowsPerBlockF32Split : kRowsPerBlockF32);
   ++g_launches;
   return hipSuccess;
 }
 hipError_t launch_fwd_mfma16(const FwdParams& p, int d, bool, bool, int waves, hipStream_t) {
   expect(d == 64 || d == 128, "head dim");
+  expect(p.key_split == 0, "key split outside fp32");
   expect(waves == 4 || waves == 8, "waves");
   check_fwd(p, 32 * waves);
   ++g_launches;

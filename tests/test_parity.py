@@ -246,7 +246,10 @@ def test_varlen_with_empty_sequences():
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])
 def test_varlen_equals_dense_per_sequence(dtype):
     # The packed entry computes exactly what the dense entry computes on each
-    # sequence alone (same kernel arithmetic, different strides): bitwise.
+    # sequence alone (same kernel arithmetic, different strides): bitwise for
+    # the 16-bit kernels. A single fp32 sequence this small runs the dense
+    # entry's key-split form, which adds the keys in another order, so fp32
+    # is compared at its tolerance.
     dev = device()
     lengths = [300, 17, 129, 64]
     H, d = 4, 128
@@ -257,6 +260,10 @@ def test_varlen_equals_dense_per_sequence(dtype):
         a = int(cu[s])
         sl = lambda t: t[a:a + n].permute(1, 0, 2).contiguous()[None]  # [1,H,n,d]
         od, ld = run_dense(sl(q), sl(k), sl(v), 0.09, dev)
+        if dtype == "fp32":
+            assert_close(f"O seq {s}", f64(od[0].permute(1, 0, 2)), f64(o[a:a + n]), TOL[dtype][0])
+            assert_close(f"L seq {s}", f64(ld[0]), f64(lse[:, a:a + n]), TOL[dtype][1])
+            continue
         assert torch.equal(od[0].permute(1, 0, 2).cpu(), o[a:a + n].cpu()), f"O seq {s}"
         assert torch.equal(ld[0].cpu(), lse[:, a:a + n].cpu()), f"L seq {s}"
 
