@@ -47,8 +47,10 @@ namespace fa {
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool varlen, hipStream_t) {
   expect(d == 64 || d == 128, "head dim");
   expect(p.key_split == 0 || (!varlen && p.key_split == f32_key_split(d)), "key split");
-  expect(p.key_split == 0 || (int64_t)((p.N + kRowsPerBlockF32 - 1) / kRowsPerBlockF32) * p.H *
-                                     p.B < kF32SplitBelowBlocks, "key split on a large grid");
+  const bool small = (int64_t)((p.N + kRowsPerBlockF32 - 1) / kRowsPerBlockF32) * p.H * p.B <
+                    kF32SplitBelowBlocks;
+  expect(p.key_split == 0 || small, "key split on a large grid");
+  expect(p.key_split > 0 || varlen || !small, "small dense fp32 grid without the key split");
   check_fwd(p, p.key_split ? kRowsPerBlockF32Split : kRowsPerBlockF32);
   ++g_launches;
   return hipSuccess;

@@ -93,7 +93,12 @@ def _collect():
     # Calls that pass validation and reach a launcher. The fake buffers sit
     # 2^40 bytes apart, so even the largest problems below do not overlap.
     far = {k: (i + 1) << 40 for i, k in enumerate(("Q", "K", "V", "O", "L"))}
-    ok_dense = [dict(), dict(N=1), dict(N=2049, d=128), dict(dtype=abi.fa.FA_F32, N=300),
+    # fp32: B*H*ceil(N/128) below 256 runs the key-split form, the stub checks
+    # which form each call takes (255 and 256 workgroups sit on either side).
+    f32 = abi.fa.FA_F32
+    ok_dense = [dict(), dict(N=1), dict(N=2049, d=128), dict(dtype=f32, N=300),
+                dict(dtype=f32, B=1, H=255, N=100), dict(dtype=f32, B=1, H=256, N=100, d=128),
+                dict(dtype=f32, B=2, H=128, N=200), dict(dtype=f32, B=1, H=1, N=1),
                 dict(B=1, H=1, N=(1 << 24) - 1, d=64), dict(B=524287, H=1, N=4096, d=64)]
     add(abi.dense, ok_dense, status=0, launches=1, **far)
     ok_varlen = [dict(), dict(maxlen=300), dict(maxlen=4097, T=9000), dict(nseq=65, T=7000),
