@@ -23,9 +23,11 @@
 //  * Ping-pong between the two waves of a SIMD: waves w and w+4 (measured:
 //    they share a SIMD) run half a step apart, and each step of a wave is a
 //    matrix half (MFMAs and LDS reads only) and a softmax half (VALU only),
-//    separated by workgroup barriers. Exponentials issued by the wave that
-//    also issues the MFMAs barely overlap them, while the VALU of one wave
-//    and the MFMAs of the other do.
+//    separated by workgroup barriers. The softmax of a tile depends on the
+//    scores the same wave has just computed, so inside one wave it would
+//    wait for them; split across the two waves, the VALU of one runs while
+//    the matrix core works for the other (measured faster than interleaving
+//    both streams in one wave).
 //  * K and V tiles travel HBM -> LDS with global_load_lds_dwordx4 (no
 //    staging registers, no LDS write instructions), issued by waves 4-7 at
 //    the start of their softmax half. Both stay row-major in LDS with an
@@ -322,8 +324,8 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
   // of tile t+1 and P.V of tile t) while the other is in its softmax half
   // (VALU only: row max, rescale, exponentials, row sums, P in the storage
   // dtype); at the next barrier they swap. The matrix core and the VALU of
-  // a SIMD thus work for different waves at the same time, which overlaps
-  // far better than MFMAs and exponentials issued by one wave.
+  // a SIMD thus work for different waves at the same time, and neither
+  // waits on the other's results.
   const bool grp_a = NW == 8 && wave < 4;  // with NW = 4 every wave is in group B
   // Packed batches: a wave whose 32 query rows all lie past the end of its
   // sequence (in the ragged last block of a sequence) computes nothing; it

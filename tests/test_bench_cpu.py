@@ -34,6 +34,14 @@ def test_pmc_reader_checks_the_source_hash(tmp_path, monkeypatch):
     assert bench.read_pmc_traffic("missing") is None
 
 
+def test_source_hash_ignores_comments_only():
+    code = "int f(int x) {\n  return x + 1;  // add one\n}\n"
+    same = "// header\n/* block\n   comment */\nint f(int x) {\n\n  return x + 1;\n}\n"
+    other = "int f(int x) {\n  return x + 2;  // add one\n}\n"
+    assert bench.source_code_text(code) == bench.source_code_text(same)
+    assert bench.source_code_text(code) != bench.source_code_text(other)
+
+
 def test_source_hash_is_per_kernel():
     hashes = {k: bench.kernel_source_hash(k) for k in bench.KERNEL_SOURCES}
     assert len(set(hashes[k] for k in ("q_outer", "kv_outer", "norm"))) == 3
