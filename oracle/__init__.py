@@ -23,6 +23,7 @@ from .attention_bwd_f64 import (  # noqa: F401
     attention_backward,
     attention_backward_lse,
     attention_backward_dense,
+    attention_backward_lse_dense,
     row_dot,
 )
 from .attention_band_f64 import (  # noqa: F401

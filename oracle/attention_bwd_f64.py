@@ -113,6 +113,19 @@ def attention_backward_dense(q, k, v, do, scale: float):
     return dq, dk, dv
 
 
+def attention_backward_lse_dense(q, k, v, o, do, lse, scale: float):
+    """[B, H, N, d] tensors and L [B, H, N]; the gradients from the given O
+    and L, head by head (attention_backward_lse)."""
+    q, k, v, o, do, lse = _f64(q), _f64(k), _f64(v), _f64(o), _f64(do), _f64(lse)
+    B, H = q.shape[:2]
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    for b in range(B):
+        for h in range(H):
+            dq[b, h], dk[b, h], dv[b, h] = attention_backward_lse(
+                q[b, h], k[b, h], v[b, h], o[b, h], do[b, h], lse[b, h], scale)
+    return dq, dk, dv
+
+
 def row_dot(dO, O):
     """D_r = sum_k dO[r,k] O[r,k] (float64), any leading shape."""
     return np.sum(_f64(dO) * _f64(O), axis=-1)

@@ -174,7 +174,8 @@ def test_poisoned_backward(d, N):
     qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
     o, lse = fwd(fa.load(), qd, kd, vd, scale)
     got = bwd(lib, qd, kd, vd, o, dod, lse, scale)
-    want = oracle.attention_backward_dense(q, k, v, do, scale)
+    # The oracle from the same O and L the backward was given.
+    want = oracle.attention_backward_lse_dense(q, k, v, f64(o), do, f64(lse), scale)
     floor = 0.1 * max(float(np.max(np.abs(w))) for w in want)
     for name, g, w in zip(("dQ", "dK", "dV"), got, want):
         bound = 1e-2 * max(float(np.max(np.abs(w))), floor)

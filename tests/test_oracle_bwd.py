@@ -138,3 +138,42 @@ def test_dense_wrapper_matches_heads():
     a = oracle.attention_backward(q[1, 2], k[1, 2], v[1, 2], g[1, 2], 0.5)
     for x, y in zip((dq[1, 2], dk[1, 2], dv[1, 2]), a):
         np.testing.assert_array_equal(x, y)
+
+
+def test_lse_dense_wrapper_matches_plain_from_exact_forward():
+    rng = np.random.default_rng(12)
+    q, k, v, g = (rng.standard_normal((2, 2, 23, 8)) for _ in range(4))
+    o = np.empty_like(q)
+    lse = np.empty(q.shape[:3])
+    for b in range(2):
+        for h in range(2):
+            o[b, h], lse[b, h] = oracle.attention_naive(q[b, h], k[b, h], v[b, h], 0.4)
+    a = oracle.attention_backward_lse_dense(q, k, v, o, g, lse, 0.4)
+    e = oracle.attention_backward_dense(q, k, v, g, 0.4)
+    for x, y in zip(a, e):
+        np.testing.assert_allclose(x, y, atol=1e-12)
+
+
+def test_lse_rendering_uses_the_given_o_and_l():
+    # D_r = sum_j dO[r,j] O[r,j] comes from the O it is given: moving O[r,j]
+    # by delta moves D_r by delta*dO[r,j], so dS[r,:] = P[r,:](dP[r,:] - D_r)
+    # moves by -P[r,:] delta dO[r,j] and dQ[r] by -scale delta dO[r,j] (P K)[r];
+    # dV = P^T dO does not move. Raising L_r by eps scales row r of P by
+    # exp(-eps), so dV moves by (exp(-eps) - 1) P[r,:]^T dO[r].
+    Q, K, V, G = _inputs(9, 13, 6, seed=13)
+    scale, r, j, delta, eps = 0.7, 4, 2, 0.01, 0.05
+    O, L = oracle.attention_naive(Q, K, V, scale)
+    base = oracle.attention_backward_lse(Q, K, V, O, G, L, scale)
+    O2 = O.copy()
+    O2[r, j] += delta
+    moved = oracle.attention_backward_lse(Q, K, V, O2, G, L, scale)
+    P = oracle.scores_to_weights(scale * Q @ K.T)[0]
+    want_dq = base[0].copy()
+    want_dq[r] -= scale * delta * G[r, j] * (P[r] @ K)
+    np.testing.assert_allclose(moved[0], want_dq, atol=1e-12)
+    np.testing.assert_allclose(moved[2], base[2], atol=1e-13)
+    L2 = L.copy()
+    L2[r] += eps
+    shifted = oracle.attention_backward_lse(Q, K, V, O, G, L2, scale)
+    np.testing.assert_allclose(shifted[2] - base[2], np.outer(P[r], G[r]) * (np.exp(-eps) - 1),
+                               atol=1e-12)

@@ -133,11 +133,12 @@ def _bwd_cases(n=12 * MULT, seed=2029):
 
 @pytest.mark.parametrize("case", _bwd_cases(), ids=lambda c: f"bwd{c[0]}-{c[1]}-d{c[2]}-N{c[5]}")
 def test_backward_sweep(case):
-    from test_parity_bwd import TOL_BWD, check_grads, run_bwd
+    from test_parity_bwd import TOL_BWD, check_grads, reference_grads, run_bwd
     i, dtype, d, B, H, N, scale = case
     dev = device()
     announce(f"sweep backward #{i}: {dtype} B={B} H={H} N={N} d={d} scale={scale:.4f}")
     q, k, v, do = workloads.dense_bwd_inputs(B, H, N, d, dtype, seed=4000 + i)
-    got = run_bwd(q, k, v, do, scale, dev)
-    want = oracle.attention_backward_dense(q, k, v, do, scale)
-    check_grads(f"sweep {i}", got, want, TOL_BWD[dtype])
+    got, fwd = run_bwd(q, k, v, do, scale, dev)
+    want = reference_grads(q, k, v, do, fwd, scale)
+    check_grads(f"sweep {i}", got, want, TOL_BWD[dtype],
+                oracle.attention_backward_dense(q, k, v, do, scale))
