@@ -49,7 +49,7 @@ import threading
 __all__ = [
     "FA_F32", "FA_F16", "FA_BF16", "FaError", "LIB_PATH", "load", "fa_fwd", "fa_fwd_varlen",
     "fa_strerror", "fa_version", "forward", "forward_varlen", "EXPORTED_SYMBOLS", "fa_bwd",
-    "fa_bwd_noalloc", "load_library", "POISON_LIB_PATH",
+    "fa_bwd_noalloc", "load_library", "POISON_LIB_PATH", "TRACE_LIB_PATH", "fa_debug_fwd_trace",
     "backward", "fa_fwd_banded", "forward_banded", "fa_fwd_kv_outer", "forward_kv_outer",
     "fa_dropout_add_norm", "dropout_add_norm", "FA_NORM_LAYER", "FA_NORM_RMS",
 ]
@@ -59,12 +59,14 @@ FA_NORM_LAYER, FA_NORM_RMS = 0, 1
 STATUS = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_HEADDIM", -4: "FA_ERR_DTYPE",
     -5: "FA_ERR_ALIGN", -6: "FA_ERR_ALIAS", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_SCALE",
-    -9: "FA_ERR_SIZE", -10: "FA_ERR_ARG", -11: "FA_ERR_SCRATCH",
+    -9: "FA_ERR_SIZE", -10: "FA_ERR_ARG", -11: "FA_ERR_SCRATCH", -12: "FA_ERR_UNSUPPORTED",
 }
 EXPORTED_SYMBOLS = ("fa_fwd", "fa_fwd_varlen", "fa_fwd_banded", "fa_fwd_kv_outer", "fa_bwd",
-                    "fa_bwd_noalloc", "fa_dropout_add_norm", "fa_strerror", "fa_version")
+                    "fa_bwd_noalloc", "fa_dropout_add_norm", "fa_debug_fwd_trace", "fa_strerror",
+                    "fa_version")
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 POISON_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_lds_poison.so")
+TRACE_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa_trace.so")
 
 _lib = None
 _lib_lock = threading.Lock()
@@ -94,7 +96,7 @@ def _load_locked() -> ctypes.CDLL:
 def load_library(path: str) -> ctypes.CDLL:
     """Load a build of the library at `path` and declare its C signatures.
     load() uses it for libfa.so; tests use it for the debug variant
-    libfa_lds_poison.so (POISON_LIB_PATH)."""
+    libfa_lds_poison.so (POISON_LIB_PATH) and libfa_trace.so (TRACE_LIB_PATH)."""
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m exact_attention_26_amd.build`")
     lib = ctypes.CDLL(path)
@@ -114,6 +116,8 @@ def load_library(path: str) -> ctypes.CDLL:
     lib.fa_bwd.restype = i32
     lib.fa_bwd_noalloc.argtypes = [vp] * 9 + [i32, i32, i32, i32, f32, i32, vp]
     lib.fa_bwd_noalloc.restype = i32
+    lib.fa_debug_fwd_trace.argtypes = [i32, vp]
+    lib.fa_debug_fwd_trace.restype = i32
     lib.fa_strerror.argtypes = [i32]
     lib.fa_strerror.restype = ctypes.c_char_p
     lib.fa_version.argtypes = []
@@ -172,6 +176,13 @@ def fa_bwd(Q, K, V, O, dO, L, dQ, dK, dV, delta, B, H, N, d, scale, dtype, strea
 def fa_bwd_noalloc(Q, K, V, O, dO, L, dQ, dK, dV, B, H, N, d, scale, dtype, stream) -> None:
     _check(load().fa_bwd_noalloc(Q, K, V, O, dO, L, dQ, dK, dV, int(B), int(H), int(N), int(d),
                                  float(scale), int(dtype), stream))
+
+
+def fa_debug_fwd_trace(workgroup, trace_buffer, lib=None) -> None:
+    """Phase trace of the 16-bit forward; implemented by the debug build
+    libfa_trace.so only (pass it as `lib`), FaError(FA_ERR_UNSUPPORTED) from
+    the product library."""
+    _check((lib or load()).fa_debug_fwd_trace(int(workgroup), trace_buffer))
 
 
 # ---------------------------------------------------------------------------

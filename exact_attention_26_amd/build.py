@@ -6,10 +6,13 @@ Every translation unit is compiled with hipcc for gfx950 only, with packed
 fp32 VALU instructions disabled, then linked into a shared library next to
 this file. Object files go to ``_build/`` at the repository root.
 
-A second library, libfa_lds_poison.so, is built from the same sources with
-FA_DEBUG_POISON_LDS: before every LDS DMA copy is issued its destination is
-filled with NaN, so a read of a stage that is not ordered after the copy's
-completion shows up as NaN in the outputs. Only the tests load it.
+Two debug libraries are built from the same sources; only the tests load
+them:
+  libfa_lds_poison.so (FA_DEBUG_POISON_LDS): before every LDS DMA copy is
+    issued its destination is filled with NaN, so a read of a stage that is
+    not ordered after the copy's completion shows up as NaN in the outputs;
+  libfa_trace.so (FA_DEBUG_TRACE): the 16-bit forward can record the
+    timestamps of each phase of one workgroup (fa_debug_fwd_trace).
 """
 from __future__ import annotations
 
@@ -24,9 +27,11 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 POISON_LIB = os.path.join(PKG, "libfa_lds_poison.so")
+TRACE_LIB = os.path.join(PKG, "libfa_trace.so")
 # Library variants: output path, extra compile flags, object directory.
 VARIANTS = [(LIB, [], BUILD),
-            (POISON_LIB, ["-DFA_DEBUG_POISON_LDS"], os.path.join(BUILD, "lds_poison"))]
+            (POISON_LIB, ["-DFA_DEBUG_POISON_LDS"], os.path.join(BUILD, "lds_poison")),
+            (TRACE_LIB, ["-DFA_DEBUG_TRACE"], os.path.join(BUILD, "trace"))]
 
 SOURCES = ["fa_api.hip", "fa_noalloc.hip", "fa_fwd_f32.hip", "fa_fwd_mfma16.hip", "fa_fwd_kvouter.hip",
            "fa_norm.hip",

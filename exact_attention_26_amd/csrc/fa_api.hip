@@ -36,7 +36,7 @@ constexpr int kVarlenNarrowMaxN = FA_VARLEN_NARROW_MAX_N;  // max_seqlen
 // Largest query block of any forward kernel (the 8-wave 16-bit one).
 constexpr int kMaxRowsPerBlock = 256;
 
-constexpr int kVersion = 600;  // 0.6.0: adds fa_bwd_noalloc
+constexpr int kVersion = 700;  // 0.7.0: adds fa_debug_fwd_trace (debug build)
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -422,6 +422,15 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
+int fa_debug_fwd_trace(int workgroup, unsigned long long* trace_buffer) {
+  if (workgroup < -1) return FA_ERR_ARG;
+  if (workgroup >= 0 && !trace_buffer) return FA_ERR_NULL;
+  if (workgroup >= 0 && (reinterpret_cast<uintptr_t>(trace_buffer) & 7u) != 0) return FA_ERR_ALIGN;
+  const hipError_t e = fa::set_fwd_trace(workgroup, trace_buffer);
+  if (e == hipErrorNotSupported) return FA_ERR_UNSUPPORTED;
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 const char* fa_strerror(int status) {
   switch (status) {
     case FA_OK: return "FA_OK: success";
@@ -436,6 +445,7 @@ const char* fa_strerror(int status) {
     case FA_ERR_SIZE: return "FA_ERR_SIZE: problem too large for 32-bit in-head offsets or one launch grid";
     case FA_ERR_ARG: return "FA_ERR_ARG: an argument outside its documented range";
     case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH: problem larger than the library's static scratch buffer";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: not available in this build of the library";
     default: return "unknown fa_status";
   }
 }

@@ -77,6 +77,32 @@ static_assert(FA_RESCALE_TAU >= 5 && FA_RESCALE_TAU <= 15, "a lane sums 2^5 valu
 #define FA_SKIP_IDLE 1
 #endif
 
+// Phase trace (debug build libfa_trace.so only, FA_DEBUG_TRACE): one chosen
+// workgroup records the shader-clock timestamp (s_memtime) of four points of
+// each of its first kTraceSteps steps, per wave: the start and end of its
+// matrix half, and the start and end of its softmax half. The points sit
+// where the wave has no LDS read in flight, since the timestamp's wait
+// (lgkmcnt) would otherwise also wait for those reads. Timestamps go to LDS
+// and are copied to the host-given buffer at the end of the workgroup,
+// followed per wave by s_memtime and the 100 MHz clock (s_memrealtime) at
+// its start and end, for the clock rate. Layout (u64): [wave][step][point]
+// for 8 waves x kTraceSteps x 4, then [wave][4].
+#ifdef FA_DEBUG_TRACE
+__device__ unsigned long long* fa_trace_buf;
+__device__ int fa_trace_wg = -1;
+#define FA_TRACE(pt, tt)                                                     \
+  do {                                                                       \
+    if (tracing && (tt) >= 0 && (tt) < fa::kTraceSteps) {                    \
+      const unsigned long long ts_ = __builtin_amdgcn_s_memtime();           \
+      if (lane == 0) trbuf[(wave * fa::kTraceSteps + (tt)) * 4 + (pt)] = ts_; \
+    }                                                                        \
+  } while (0)
+#else
+#define FA_TRACE(pt, tt) \
+  do {                   \
+  } while (0)
+#endif
+
 namespace fa {
 namespace {
 
@@ -124,6 +150,15 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
 
   WorkUnit u;
   if (!resolve_unit<VARLEN>(p, BR, u)) return;
+#ifdef FA_DEBUG_TRACE
+  __shared__ unsigned long long trbuf[8 * kTraceSteps * 4];
+  const bool tracing = (int)blockIdx.x == fa_trace_wg;
+  unsigned long long trace_t0 = 0, trace_r0 = 0;
+  if (tracing) {
+    trace_t0 = __builtin_amdgcn_s_memtime();
+    trace_r0 = __builtin_amdgcn_s_memrealtime();
+  }
+#endif
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -531,14 +566,18 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
     using VS = std::integral_constant<int, F>;
     using KN = std::integral_constant<int, (F + 2) % S>;
     using VN = std::integral_constant<int, (F + 1) % S>;
+    FA_TRACE(0, t);
     if (busy) matrix(has_next, KS{}, VS{});
+    FA_TRACE(1, t);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    FA_TRACE(2, t);
     if constexpr (decltype(has_next)::value) {
       if (busy) preread(KN::value, VN::value);
       if (!grp_a) copies(KS{}, VS{}, t);
       if (busy) softmax(LoopForm{}, t + 1 == rag, (t0 + t + 1) * BC);
     }
+    FA_TRACE(3, t);
     __syncthreads();
   };
 
@@ -665,6 +704,18 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
     }
     if (qrow < n && g == 0) p.lse[u.lse_base + qrow] = m * p.scale + logf(l);
   }
+#ifdef FA_DEBUG_TRACE
+  if (tracing) {
+    const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+    const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+    unsigned long long* out = fa_trace_buf;
+    for (int i = lane; i < kTraceSteps * 4; i += 64)
+      out[wave * kTraceSteps * 4 + i] = trbuf[wave * kTraceSteps * 4 + i];
+    if (lane < 4)
+      out[8 * kTraceSteps * 4 + wave * 4 + lane] =
+          lane == 0 ? trace_t0 : lane == 1 ? trace_r0 : lane == 2 ? t1 : r1;
+  }
+#endif
 }
 
 template <bool BF16, int D>
@@ -680,6 +731,18 @@ const void* pick(bool varlen, bool band, int waves) {
 }
 
 }  // namespace
+
+hipError_t set_fwd_trace(int workgroup, unsigned long long* buffer) {
+#ifdef FA_DEBUG_TRACE
+  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(fa_trace_buf), &buffer, sizeof(buffer));
+  if (e == hipSuccess) e = hipMemcpyToSymbol(HIP_SYMBOL(fa_trace_wg), &workgroup, sizeof(workgroup));
+  return e;
+#else
+  (void)workgroup;
+  (void)buffer;
+  return hipErrorNotSupported;
+#endif
+}
 
 hipError_t launch_fwd_mfma16(const FwdParams& p, int d, bool bf16, bool varlen, int waves,
                              hipStream_t stream) {

@@ -53,6 +53,11 @@ inline int64_t fwd_grid(const FwdParams& p) {
 
 // Launchers; return 0 on success or a hipError_t from the launch.
 hipError_t launch_fwd_f32(const FwdParams& p, int d, bool varlen, hipStream_t stream);
+// Phase trace of the 16-bit forward (debug build only): steps recorded per
+// wave, and the setter; workgroup -1 turns it off. Without FA_DEBUG_TRACE the
+// setter returns hipErrorNotSupported.
+constexpr int kTraceSteps = 64;
+hipError_t set_fwd_trace(int workgroup, unsigned long long* buffer);
 // waves: 8 (ping-pong, 256-row workgroups) or 4 (one wave group, 128-row
 // workgroups); p.q_blocks must count blocks of 32 * waves rows.
 hipError_t launch_fwd_mfma16(const FwdParams& p, int d, bool bf16, bool varlen, int waves,

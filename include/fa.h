@@ -70,7 +70,8 @@ typedef enum {
   FA_ERR_SCALE = -8,    /* scale not finite or not > 0                       */
   FA_ERR_SIZE = -9,     /* too large for 32-bit in-head offsets or one grid  */
   FA_ERR_ARG = -10,     /* an argument outside its documented range          */
-  FA_ERR_SCRATCH = -11  /* larger than the library's static scratch buffer    */
+  FA_ERR_SCRATCH = -11, /* larger than the library's static scratch buffer    */
+  FA_ERR_UNSUPPORTED = -12 /* not available in this build of the library       */
 } fa_status;
 
 typedef enum {
@@ -283,6 +284,32 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
 int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                    const float* L, void* dQ, void* dK, void* dV,
                    int B, int H, int N, int d, float scale, int dtype, void* stream);
+
+/*
+ * Phase trace of the 16-bit forward, for performance work. Only the debug
+ * build libfa_trace.so (compiled with FA_DEBUG_TRACE) implements it; the
+ * product library returns FA_ERR_UNSUPPORTED and records nothing.
+ *
+ * After this call, every fa_fwd / fa_fwd_varlen / fa_fwd_banded launch of the
+ * 16-bit kernel has its workgroup number `workgroup` (launch order, as
+ * blockIdx.x) record, per wave and for each of its first 64 key-tile steps,
+ * the shader-clock timestamps (s_memtime) of the start and end of the wave's
+ * matrix half and of its softmax half, and write them to `trace_buffer` when
+ * it ends. Later launches overwrite the buffer. workgroup = -1 turns the
+ * trace off.
+ *   trace_buffer : device memory of at least 2080 uint64 values, 8-byte
+ *                  aligned, owned by the caller: [wave 0..7][step 0..63]
+ *                  [point 0..3], then per wave {s_memtime at the start,
+ *                  s_memrealtime (100 MHz) at the start, s_memtime at the
+ *                  end, s_memrealtime at the end}. Waves and steps that do not
+ *                  exist keep their old contents.
+ * The call is synchronous (it copies two values to device symbols) and is
+ * not ordered with work already enqueued. Returns FA_ERR_NULL for a NULL
+ * buffer with workgroup >= 0, FA_ERR_ALIGN for a misaligned one, FA_ERR_ARG
+ * for workgroup < -1, FA_ERR_UNSUPPORTED in the product library,
+ * FA_ERR_LAUNCH when the copies fail, else FA_OK.
+ */
+int fa_debug_fwd_trace(int workgroup, unsigned long long* trace_buffer);
 
 /* Static, NUL-terminated description of an fa_status value. */
 const char* fa_strerror(int status);

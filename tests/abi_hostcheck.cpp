@@ -84,6 +84,8 @@ hipError_t launch_bwd(const BwdParams& p, int d, bool, hipStream_t) {
   return hipSuccess;
 }
 
+hipError_t set_fwd_trace(int, unsigned long long*) { return hipErrorNotSupported; }
+
 }  // namespace fa
 
 namespace {
@@ -159,6 +161,11 @@ int call(const std::string& fn, Args& a) {
     return (s && std::strlen(s) > 0) ? 0 : -1000;
   }
   if (fn == "fa_version") return fa_version();
+  if (fn == "fa_debug_fwd_trace") {
+    int wg = a.in();
+    void* buf = a.ptr();
+    return fa_debug_fwd_trace(wg, (unsigned long long*)buf);
+  }
   std::fprintf(stderr, "unknown function %s\n", fn.c_str());
   std::abort();
 }

@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert fa.fa_version() == 600
+    assert fa.fa_version() == 700
     for code, name in fa.STATUS.items():
         assert fa.fa_strerror(code).startswith(name)
     assert fa.fa_strerror(12345) == "unknown fa_status"
@@ -313,3 +313,14 @@ def test_norm_optional_pointers_accepted_as_null(lib):
     # passes, then an empty problem launches nothing
     assert norm(lib, rows=0, x1=0, res=0, b0=0, g1=0, b1=0, y1=0, z=0, mean=0, rstd=0,
                 mask=0) == 0
+
+
+# fa_debug_fwd_trace: validation, then FA_ERR_UNSUPPORTED from the product
+# library (only the debug build libfa_trace.so records a trace).
+TRACE_CASES = [((-2, 0x1000), -10), ((0, None), -1), ((3, 0x1004), -5),
+               ((-1, None), -12), ((0, 0x1000), -12), ((5, 0x1008), -12)]
+
+
+@pytest.mark.parametrize("args,status", TRACE_CASES)
+def test_debug_trace_is_debug_build_only(lib, args, status):
+    assert lib.fa_debug_fwd_trace(*args) == status

@@ -118,9 +118,11 @@ def _collect():
         launches=1, **far_nm)
     add(abi.norm, [dict(x1=0, res=0, g1=0, b1=0, y1=0, z=0, mean=0, rstd=0, mask=0)], status=0,
         launches=1, **{k: v for k, v in far_nm.items()})
+    for args, st in abi.TRACE_CASES:
+        expect.append((rec.fa_debug_fwd_trace(*args), st, 0))
     for code in list(abi.fa.STATUS) + [12345]:
         expect.append((rec.fa_strerror(code), 0, 0))
-    expect.append((rec.fa_version(), 600, 0))
+    expect.append((rec.fa_version(), 700, 0))
     return rec.calls, expect
 
 
