@@ -18,7 +18,10 @@ namespace {
 // - banded: faster from w = 0 (1.56x) to w = 2048 (1.02x), slower from 4096;
 // - dense: d = 64, N = 512 +12 %, N = 2048 +10 %; d = 128, N = 1024 +5 %,
 //   N = 4096 -2 %, N = 8192 -3 %;
-// - varlen: lengths 64..4096 +4 %, 64..1024 +29 %.
+// - varlen, 32 sequences of lengths drawn from a range (d = 128): 64..1024
+//   +6 %, 64..2048 +1.7 %, 64..2560 and 64..3072 within 0.3 %, 64..4096,
+//   1024..4096 and 2048..4096 -1.4 %; packed batches switch to 8 waves
+//   above max_seqlen 3072.
 #ifndef FA_BAND_NARROW_MAX
 #define FA_BAND_NARROW_MAX 2048
 #endif
@@ -26,7 +29,7 @@ namespace {
 #define FA_DENSE_NARROW_MAX_N 2048
 #endif
 #ifndef FA_VARLEN_NARROW_MAX_N
-#define FA_VARLEN_NARROW_MAX_N 4096
+#define FA_VARLEN_NARROW_MAX_N 3072
 #endif
 constexpr int kWavesPingPong = 8;
 constexpr int kWavesNarrow = 4;

@@ -204,8 +204,24 @@ __global__ __launch_bounds__(64 * NW, 2) void fwd16_kernel(FwdParams p) {
     const int pos = s % T::KCHUNKS;
     return ((((pos >> 2) ^ T::vswz(s / T::KCHUNKS)) << 2) | (pos & 3)) * 8;
   };
-#define FA_KOFF(r) ((unsigned)(dma_row(r) * rs + dma_kcol(r)) * 2u)
-#define FA_VOFF(r) ((unsigned)(dma_row(r) * rs + dma_vcol(r)) * 2u)
+  // Byte offsets of the full-tile copies relative to the tile's first row.
+  // They do not change over the loop; computed once and pinned in registers
+  // (opaque to the compiler, which would otherwise recompute them before
+  // every copy: ~4 VALU instructions each, one a quarter-rate multiply, in
+  // the copying waves' softmax half). Where that would push the kernel past
+  // 256 VGPRs (4-wave packed d = 128, banded d = 128) they are recomputed.
+  constexpr bool PRE_OFF = !(D == 128 && (BAND || (VARLEN && NW == 4)));
+  unsigned koff[PRE_OFF ? NDMA : 1], voff[PRE_OFF ? NDMA : 1];
+  if constexpr (PRE_OFF) {
+#pragma unroll
+    for (int r = 0; r < NDMA; ++r) {
+      koff[r] = (unsigned)(dma_row(r) * rs + dma_kcol(r)) * 2u;
+      voff[r] = (unsigned)(dma_row(r) * rs + dma_vcol(r)) * 2u;
+      __asm__ volatile("" : "+v"(koff[r]), "+v"(voff[r]));
+    }
+  }
+#define FA_KOFF(r) (PRE_OFF ? koff[PRE_OFF ? (r) : 0] : (unsigned)(dma_row(r) * rs + dma_kcol(r)) * 2u)
+#define FA_VOFF(r) (PRE_OFF ? voff[PRE_OFF ? (r) : 0] : (unsigned)(dma_row(r) * rs + dma_vcol(r)) * 2u)
   const unsigned lds0 = (unsigned)(uintptr_t)(lds_u8*)lds + (unsigned)(dwave * NDMA * 1024);
   // Copy the K (or V) tile at key kb into LDS at byte `dst`. In the ragged
   // last tile (tail) rows past the end are clamped to row n-1: loads stay in

@@ -2,8 +2,8 @@
 workgroups) forms of the 16-bit forward run the same steps per wave on the
 same 32 query rows and the same key tiles in the same order, so they must
 give bitwise-identical O and L. The library picks the form by size: dense
-N <= 2048 and packed batches with max_seqlen <= 4096 run 4 waves, larger
-problems 8. A packed batch with one sequence longer than 4096 runs 8 waves
+N <= 2048 and packed batches with max_seqlen <= 3072 run 4 waves, larger
+problems 8. A packed batch with one sequence longer than 3072 runs 8 waves
 for every sequence; each of its shorter sequences is then compared bit for
 bit with a dense call on that sequence alone, which runs 4 waves. The
 lengths cover one to many key tiles, ragged tails and whole tiles, so the
