@@ -113,7 +113,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
     for (int i = 0; i < 8; ++i) acc = fmaf((float)va[i], (float)vb[i], acc);
   }
   acc = lanes_sum<LPR>(acc);  // the LPR lanes of a row are an aligned group
-  if (row < p.rows && part == 0) p.delta[row] = acc;
+  // Stored negated: the key-block kernel starts its dP accumulators at -D,
+  // so its MFMAs produce dP - D directly.
+  if (row < p.rows && part == 0) p.delta[row] = -acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -150,6 +152,11 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
         vec8, *(const u32x4*)((const unsigned short*)p.k + hb + (int64_t)krc * D + 16 * s + 8 * g));
     vf[s] = __builtin_bit_cast(
         vec8, *(const u32x4*)((const unsigned short*)p.v + hb + (int64_t)krc * D + 16 * s + 8 * g));
+    // d = 128 runs one wave per SIMD with more than 256 live registers: the
+    // fragments are pinned to AGPRs (MFMA operands may come from there).
+    // Otherwise the compiler kept them in AGPRs but copied every one to
+    // another AGPR before each use (56 moves per tile).
+    if constexpr (D == 128) __asm__ volatile("" : "+a"(kf[s]), "+a"(vf[s]));
   }
   f32x16 dk[D / 32], dv[D / 32];  // dK^T, dV^T: d = 32t + 8(i/4) + 4g + i%4, key l32
 #pragma unroll
@@ -193,14 +200,27 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
   const float c2 = p.scale_log2;
   constexpr float kLog2e = 1.4426950408889634f;
 
-  auto compute = [&](int st, int q0) {
+  // RAG (compile time): the tile holds queries past the end (only the last
+  // tile can); full tiles carry no masking code at all. Left as a runtime
+  // test, the compiler turned the mask into selects executed on every tile.
+  auto compute = [&](auto stage, int q0, auto rag) {
+    constexpr bool RAG = decltype(rag)::value;
+    const int st = stage;
     const lds_u8* Qs = (const lds_u8*)lds + st * STG;
     const lds_u8* Os = Qs + T::TILEB;
     const float* Ls = (const float*)(lds + st * STG + 2 * T::TILEB);
     const float* Ds = Ls + 64;
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {  // 32-query halves of the tile
-      f32x16 s = {}, dp = {};         // rows: query hq*32 + 8(i/4) + 4g + i%4; column: key l32
+      // rows: query hq*32 + 8(i/4) + 4g + i%4; column: key l32. dp starts
+      // at -D of its row (the scratch holds -D), so it ends as dP - D.
+      f32x16 s = {}, dp;
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 nd = *(const f32x4*)(Ds + hq * 32 + 8 * a + 4 * g);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[4 * a + e] = nd[e];
+      }
       {
         // Q and dO row operands read two k-steps ahead of their MFMAs.
         constexpr int NS = D / 16;
@@ -224,12 +244,10 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
       // Exponent arguments, exponentials, then dS, as three fenced groups so
       // that no instruction waits right behind the exponential it consumes.
       float pr[16], ds[16];
-      f32x4 dvq[4];
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int qi = hq * 32 + 8 * a + 4 * g;
         const f32x4 lv = *(const f32x4*)(Ls + qi);
-        dvq[a] = *(const f32x4*)(Ds + qi);
 #pragma unroll
         for (int e = 0; e < 4; ++e) pr[4 * a + e] = fmaf(s[4 * a + e], c2, -lv[e] * kLog2e);
       }
@@ -243,8 +261,8 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * a + e;
-          if (q0 + qi + e >= n) pr[i] = 0.f;  // query past the end
-          ds[i] = pr[i] * (dp[i] - dvq[a][e]);
+          if (RAG && q0 + qi + e >= n) pr[i] = 0.f;  // query past the end
+          ds[i] = pr[i] * dp[i];
         }
       }
       // P and dS as B operands: slot jj of lane group g in product t is
@@ -298,12 +316,30 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
   fetch(0, 0);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int jt = 0; jt < tiles; ++jt) {
-    if (jt + 1 < tiles) fetch((jt + 1) & 1, jt + 1);  // that stage was last read in jt-1
-    compute(jt & 1, jt * TQ);
+  // Tile jt sits in stage jt & 1. The loop runs two tiles per iteration so
+  // that each stage is a compile-time constant and every LDS read address is
+  // a fixed per-lane base plus an instruction offset (a runtime stage cost
+  // one add per read). Each fetch fills the stage last read in the tile
+  // before.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  const std::false_type full;
+  auto step = [&](auto st, int jt) {
+    fetch(1 - decltype(st)::value, jt + 1);
+    compute(st, jt * TQ, full);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  int jt = 0;
+  for (; jt + 2 < tiles; jt += 2) {
+    step(S0{}, jt);
+    step(S1{}, jt + 1);
   }
+  if (jt + 1 < tiles) step(S0{}, jt++);
+  if (n % TQ == 0)
+    compute(jt & 1, jt * TQ, full);
+  else
+    compute(jt & 1, jt * TQ, std::true_type{});
 
   if (kr < n) {
     unsigned short* dkr = (unsigned short*)p.dk + hb + (int64_t)kr * D;
@@ -358,7 +394,7 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2))) 
   }
   const int qrc = min(qr, n - 1);
   const float lq = p.lse[(int64_t)bh * n + qrc] * 1.4426950408889634f;
-  const float dq_d = p.delta[(int64_t)bh * n + qrc];
+  const float dq_nd = p.delta[(int64_t)bh * n + qrc];  // -D of this query
   f32x16 acc[D / 32];  // dQ^T: d = 32t + 8(i/4) + 4g + i%4, query l32
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
@@ -388,7 +424,11 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2))) 
   const int vin = 32 * (vb & 1) + 8 * (vj & 3);
   const float c2 = p.scale_log2;
 
-  auto compute = [&](int st, int k0) {
+  // RAG (compile time): the tile holds keys past the end (only the last
+  // tile can), as in the key-block kernel.
+  auto compute = [&](auto stage, int k0, auto rag) {
+    constexpr bool RAG = decltype(rag)::value;
+    const int st = stage;
     const lds_u8* Ks = (const lds_u8*)lds + st * STG;
     const lds_u8* Vs = Ks + T::TILEB;
     f32x16 s[2] = {}, dp[2] = {};  // rows: key kt*32 + 8(i/4) + 4g + i%4; column: query l32
@@ -402,7 +442,6 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2))) 
         s[kt] = mfma32x32x16<BF16>(ka, qf[ss], s[kt]);
         dp[kt] = mfma32x32x16<BF16>(va, of[ss], dp[kt]);
       }
-    const bool ragged = k0 + TK > n;
     // P^T then dS^T, one 32-key half at a time: the half's exponent arguments,
     // its exponentials, then its dS, as three fenced groups, so no instruction
     // waits right behind the exponential it consumes.
@@ -426,11 +465,11 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2))) 
           for (int e = 0; e < 2; ++e) {
             const int i = 8 * h + 2 * q + e;
             float pv = pe[i];
-            if (ragged) {
+            if constexpr (RAG) {
               const int key = k0 + kt * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
               if (key >= n) pv = 0.f;
             }
-            x[e] = pv * (dp[kt][i] - dq_d);
+            x[e] = pv * (dp[kt][i] + dq_nd);
           }
           w[q] = pack2<BF16>(x[0], x[1]);
         }
@@ -458,12 +497,27 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2))) 
   fetch(0, 0);
   __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int kt = 0; kt < tiles; ++kt) {
-    if (kt + 1 < tiles) fetch((kt + 1) & 1, kt + 1);  // that stage was last read in kt-1
-    compute(kt & 1, kt * TK);
+  // Two tiles per iteration, each stage a compile-time constant (as in the
+  // key-block kernel).
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  const std::false_type full;
+  auto step = [&](auto st, int kt) {
+    fetch(1 - decltype(st)::value, kt + 1);
+    compute(st, kt * TK, full);
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  int kt = 0;
+  for (; kt + 2 < tiles; kt += 2) {
+    step(S0{}, kt);
+    step(S1{}, kt + 1);
   }
+  if (kt + 1 < tiles) step(S0{}, kt++);
+  if (n % TK == 0)
+    compute(kt & 1, kt * TK, full);
+  else
+    compute(kt & 1, kt * TK, std::true_type{});
 
   // The query row again, from the lane count rather than the thread index, so
   // that no per-lane address stays live (and spills) across the key loop.

@@ -1,4 +1,4 @@
-// fa_bwd_noalloc (include/fa.h): the dense backward with its D = rowsum(dO*O)
+// fa_bwd_noalloc (include/fa.h): the dense backward with its -D = -rowsum(dO*O)
 // scratch in a static device array of the library instead of a caller
 // buffer, for callers that cannot allocate device memory.
 //

@@ -243,7 +243,8 @@ int fa_dropout_add_norm(const void* x0, const void* x1, const void* residual,
  *   L              : contiguous [B, H, N] float32, natural-log logsumexp.
  *   dQ, dK, dV     : contiguous [B, H, N, d] tensors of `dtype`, written.
  *   delta          : contiguous [B, H, N] float32 scratch owned by the
- *                    caller; receives D. Its contents on entry are ignored.
+ *                    caller; receives -D (negated, the form the kernels
+ *                    consume). Its contents on entry are ignored.
  *   dtype          : FA_F16 or FA_BF16 (FA_ERR_DTYPE otherwise: there is no
  *                    fp32 backward).
  * Arithmetic: products of dtype values summed in fp32; P and dS rounded to
@@ -262,8 +263,8 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
  * Dense backward that allocates nothing: fa_bwd without the delta argument,
  * for callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc). The same
- * kernels compute the same dQ, dK, dV, bit for bit; D = rowsum(dO * O) goes
- * to a static device array of the library instead of caller scratch.
+ * kernels compute the same dQ, dK, dV, bit for bit; -D = -rowsum(dO * O)
+ * goes to a static device array of the library instead of caller scratch.
  *   - The array holds 2^22 float32 values (16 MiB): B*H*N must be at most
  *     4,194,304 (FA_ERR_SCRATCH otherwise, before anything is enqueued).
  *     Each GPU the library runs on holds its own copy from the first call on
