@@ -210,6 +210,34 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
     const lds_u8* Os = Qs + T::TILEB;
     const float* Ls = (const float*)(lds + st * STG + 2 * T::TILEB);
     const float* Ds = Ls + 64;
+    // Operand rings of the two MFMA chains of a 32-query half, read two
+    // steps ahead of their MFMAs: Q / dO rows for S and dP (step ss), and
+    // dO^T / Q^T (transposed reads) for dV and dK (step k). The first two
+    // reads of each chain are issued early, where their latency hides: the
+    // transposed ones before the softmax VALU work, the row reads of the
+    // second half during the first half's dV/dK chain. One wave per SIMD
+    // leaves nothing else to cover an LDS read at the head of a chain.
+    constexpr int NS = D / 16;
+    constexpr int NST = 2 * (D / 32);
+    vec8 qa[3], oa[3];
+    i16x4 ho[3][2], hqv[3][2];
+    auto rd_row = [&](int hq, int ss) {
+      const int r = hq * 32 + l32, cb = (2 * ss + g) * 16;
+      qa[ss % 3] = *(const __attribute__((address_space(3))) vec8*)(Qs + T::off(r, cb));
+      oa[ss % 3] = *(const __attribute__((address_space(3))) vec8*)(Os + T::off(r, cb));
+    };
+    auto rd_tr = [&](int hq, int k) {
+      const int t = k / (D / 32), dt = k % (D / 32);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int r = hq * 32 + 16 * t + 8 * h + vrow;
+        const int o = T::off(r, 64 * dt + vin);
+        ho[k % 3][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Os + o));
+        hqv[k % 3][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Qs + o));
+      }
+    };
+    rd_row(0, 0);
+    rd_row(0, 1);
 #pragma unroll
     for (int hq = 0; hq < 2; ++hq) {  // 32-query halves of the tile
       // rows: query hq*32 + 8(i/4) + 4g + i%4; column: key l32. dp starts
@@ -221,26 +249,16 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) dp[4 * a + e] = nd[e];
       }
-      {
-        // Q and dO row operands read two k-steps ahead of their MFMAs.
-        constexpr int NS = D / 16;
-        vec8 qa[3], oa[3];
-        auto rd = [&](int ss) {
-          const int r = hq * 32 + l32, cb = (2 * ss + g) * 16;
-          qa[ss % 3] = *(const __attribute__((address_space(3))) vec8*)(Qs + T::off(r, cb));
-          oa[ss % 3] = *(const __attribute__((address_space(3))) vec8*)(Os + T::off(r, cb));
-        };
-        rd(0);
-        rd(1);
 #pragma unroll
-        for (int ss = 0; ss < NS; ++ss) {
-          if (ss + 2 < NS) rd(ss + 2);
-          __builtin_amdgcn_sched_barrier(0);
-          s = mfma32x32x16<BF16>(qa[ss % 3], kf[ss], s);
-          dp = mfma32x32x16<BF16>(oa[ss % 3], vf[ss], dp);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int ss = 0; ss < NS; ++ss) {
+        if (ss + 2 < NS) rd_row(hq, ss + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        s = mfma32x32x16<BF16>(qa[ss % 3], kf[ss], s);
+        dp = mfma32x32x16<BF16>(oa[ss % 3], vf[ss], dp);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      rd_tr(hq, 0);
+      rd_tr(hq, 1);
       // Exponent arguments, exponentials, then dS, as three fenced groups so
       // that no instruction waits right behind the exponential it consumes.
       float pr[16], ds[16];
@@ -279,35 +297,21 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
         pp[t] = __builtin_bit_cast(vec8, w1);
         pd[t] = __builtin_bit_cast(vec8, w2);
       }
-      {
-        // dO^T and Q^T operands (transposed reads) two steps ahead of their MFMAs.
-        constexpr int NST = 2 * (D / 32);
-        i16x4 ho[3][2], hqv[3][2];
-        auto rd = [&](int k) {
-          const int t = k / (D / 32), dt = k % (D / 32);
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int r = hq * 32 + 16 * t + 8 * h + vrow;
-            const int o = T::off(r, 64 * dt + vin);
-            ho[k % 3][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Os + o));
-            hqv[k % 3][h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Qs + o));
-          }
-        };
-        rd(0);
-        rd(1);
-#pragma unroll
-        for (int k = 0; k < NST; ++k) {
-          const int t = k / (D / 32), dt = k % (D / 32);
-          if (k + 2 < NST) rd(k + 2);
-          __builtin_amdgcn_sched_barrier(0);
-          const i16x8 ao = {ho[k % 3][0][0], ho[k % 3][0][1], ho[k % 3][0][2], ho[k % 3][0][3],
-                            ho[k % 3][1][0], ho[k % 3][1][1], ho[k % 3][1][2], ho[k % 3][1][3]};
-          const i16x8 aq = {hqv[k % 3][0][0], hqv[k % 3][0][1], hqv[k % 3][0][2], hqv[k % 3][0][3],
-                            hqv[k % 3][1][0], hqv[k % 3][1][1], hqv[k % 3][1][2], hqv[k % 3][1][3]};
-          dv[dt] = mfma32x32x16<BF16>(__builtin_bit_cast(vec8, ao), pp[t], dv[dt]);
-          dk[dt] = mfma32x32x16<BF16>(__builtin_bit_cast(vec8, aq), pd[t], dk[dt]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int k = 0; k < NST; ++k) {
+        const int t = k / (D / 32), dt = k % (D / 32);
+        if (k + 2 < NST)
+          rd_tr(hq, k + 2);
+        else if (hq == 0)
+          rd_row(1, k + 2 - NST);  // the second half's first row operands
+        __builtin_amdgcn_sched_barrier(0);
+        const i16x8 ao = {ho[k % 3][0][0], ho[k % 3][0][1], ho[k % 3][0][2], ho[k % 3][0][3],
+                          ho[k % 3][1][0], ho[k % 3][1][1], ho[k % 3][1][2], ho[k % 3][1][3]};
+        const i16x8 aq = {hqv[k % 3][0][0], hqv[k % 3][0][1], hqv[k % 3][0][2], hqv[k % 3][0][3],
+                          hqv[k % 3][1][0], hqv[k % 3][1][1], hqv[k % 3][1][2], hqv[k % 3][1][3]};
+        dv[dt] = mfma32x32x16<BF16>(__builtin_bit_cast(vec8, ao), pp[t], dv[dt]);
+        dk[dt] = mfma32x32x16<BF16>(__builtin_bit_cast(vec8, aq), pd[t], dk[dt]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
