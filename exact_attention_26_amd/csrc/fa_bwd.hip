@@ -8,7 +8,9 @@
 // dK = dS^T Q, dQ = dS K), with dS = P * (dP - D) and D = rowsum(dO * O).
 //
 // Three kernels, enqueued in order on one stream:
-//  1. delta: D[r] = sum_k dO[r,k] O[r,k] (fp32), one pass over O and dO.
+//  1. delta: D[r] = sum_k dO[r,k] O[r,k] (fp32), one pass over O and dO;
+//     it stores -D, and -L[r]*log2 e into the dQ buffer (free until step 3
+//     writes dQ), the two per-row offsets the dK/dV kernel adds.
 //  2. dK/dV: a workgroup owns 128 keys of one head (4 waves x 32 keys) and
 //     streams the head's queries in tiles of 64. Per tile and wave:
 //       S  = Q K^T  and  dP = dO V^T   (queries x keys; A = Q / dO rows from
@@ -114,8 +116,15 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
   }
   acc = lanes_sum<LPR>(acc);  // the LPR lanes of a row are an aligned group
   // Stored negated: the key-block kernel starts its dP accumulators at -D,
-  // so its MFMAs produce dP - D directly.
-  if (row < p.rows && part == 0) p.delta[row] = -acc;
+  // so its MFMAs produce dP - D directly. The same kernel needs -L*log2(e)
+  // per query as its exponent offset; that goes to the first B*H*N floats
+  // of the dQ buffer, which nothing reads and the dQ kernel (last in the
+  // stream) overwrites with dQ. dQ holds B*H*N*d 16-bit values (d >= 64),
+  // far more than B*H*N floats.
+  if (row < p.rows && part == 0) {
+    p.delta[row] = -acc;
+    ((float*)p.dq)[row] = -p.lse[row] * 1.4426950408889634f;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -137,7 +146,7 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
   const int64_t hb = (int64_t)bh * p.head_stride;
   const unsigned short* Qg = (const unsigned short*)p.q + hb;
   const unsigned short* Og = (const unsigned short*)p.dout + hb;
-  const float* Lg = p.lse + (int64_t)bh * n;
+  const float* Lg = (const float*)p.dq + (int64_t)bh * n;  // -L*log2(e), staged by the delta kernel
   const float* Dg = p.delta + (int64_t)bh * n;
 
   // K and V rows of this lane's key as B operands (k = d): elements
@@ -198,7 +207,6 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
   const int vrow = 4 * (vb >> 1) + (vj >> 2);
   const int vin = 32 * (vb & 1) + 8 * (vj & 3);
   const float c2 = p.scale_log2;
-  constexpr float kLog2e = 1.4426950408889634f;
 
   // RAG (compile time): the tile holds queries past the end (only the last
   // tile can); full tiles carry no masking code at all. Left as a runtime
@@ -265,9 +273,9 @@ __global__ __launch_bounds__(kThreadsB) void bwd_dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int qi = hq * 32 + 8 * a + 4 * g;
-        const f32x4 lv = *(const f32x4*)(Ls + qi);
+        const f32x4 nl = *(const f32x4*)(Ls + qi);  // -L*log2(e)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pr[4 * a + e] = fmaf(s[4 * a + e], c2, -lv[e] * kLog2e);
+        for (int e = 0; e < 4; ++e) pr[4 * a + e] = fmaf(s[4 * a + e], c2, nl[e]);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
