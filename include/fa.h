@@ -242,6 +242,8 @@ int fa_dropout_add_norm(const void* x0, const void* x1, const void* residual,
  *                    fa_fwd wrote them for the same Q, K, V and scale.
  *   L              : contiguous [B, H, N] float32, natural-log logsumexp.
  *   dQ, dK, dV     : contiguous [B, H, N, d] tensors of `dtype`, written.
+ *                    The first B*H*N*4 bytes of dQ also hold a per-row
+ *                    intermediate before dQ itself is written (last).
  *   delta          : contiguous [B, H, N] float32 scratch owned by the
  *                    caller; receives -D (negated, the form the kernels
  *                    consume). Its contents on entry are ignored.
