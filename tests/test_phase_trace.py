@@ -83,3 +83,55 @@ def test_phase_trace_of_the_long_forward():
     last_b2 = int(np.sum(pts[4:, s, 1].max(0) > pts[:4, s, 3].max(0)))
     print(f"[trace] group B last at the barrier after A's matrix half: {last_b1} of {STEPS - 9}; "
           f"after B's matrix half: {last_b2} of {STEPS - 9}", flush=True)
+
+
+WAVES_NARROW = 4
+STEPS_SHORT = 16  # key tiles of N = 1024
+
+
+def test_phase_trace_of_a_short_forward():
+    """The 4-wave kernel at the short shape (B=4 H=16 N=1024 d=64 bf16: 512
+    workgroups of 128 rows, two per CU): one workgroup of each of the two
+    that share a CU. Besides the bitwise and ordering checks, no matrix half
+    may be shorter than its MFMAs (16, or 8 in the last step, of 32 clocks). Printed per workgroup: the
+    prologue (wave start to the first matrix half), the median step and its
+    matrix and softmax halves, and the write-back (last matrix half to the
+    wave's end)."""
+    dev = device()
+    B, H, N, d = 4, 16, 1024, 64
+    q, k, v = (workloads.device_normal((B, H, N, d), "bf16", seed=s, device=dev) for s in (1, 2, 3))
+    scale = d ** -0.5
+    tlib = fa.load_library(fa.TRACE_LIB_PATH)
+    o_p, l_p = _fwd(fa.load(), q, k, v, scale)
+    for wg in (100, 300):
+        announce(f"phase trace bf16 B={B} H={H} N={N} d={d}, workgroup {wg}")
+        buf = torch.zeros(WAVES * STEPS * 4 + WAVES * 4, dtype=torch.int64, device=dev)
+        fa.fa_debug_fwd_trace(wg, buf.data_ptr(), lib=tlib)
+        try:
+            for _ in range(3):
+                o_t, l_t = _fwd(tlib, q, k, v, scale)
+            torch.cuda.synchronize()
+        finally:
+            fa.fa_debug_fwd_trace(-1, None, lib=tlib)
+        assert torch.equal(o_t, o_p) and torch.equal(l_t, l_p)
+        t = buf.cpu().numpy().astype(np.float64)
+        pts = t[:WAVES * STEPS * 4].reshape(WAVES, STEPS, 4)[:WAVES_NARROW, :STEPS_SHORT]
+        cal = t[WAVES * STEPS * 4:].reshape(WAVES, 4)[:WAVES_NARROW]
+        mhz = float(np.median((cal[:, 2] - cal[:, 0]) / (cal[:, 3] - cal[:, 1]) * 100.0))
+        # The last step has no softmax half: its points 2 and 3 follow point 1.
+        assert np.all(np.diff(pts.reshape(WAVES_NARROW, -1), axis=1) >= 0), "timestamps out of order"
+        assert np.all(pts[:, 0, 0] >= cal[:, 0]) and np.all(cal[:, 2] >= pts[:, -1, 3])
+        matrix = pts[:, :, 1] - pts[:, :, 0]
+        # 16 MFMAs per matrix half (S^T of the next tile and P.V); the last
+        # has no next tile, so only its 8 P.V MFMAs.
+        assert matrix[:, :-1].min() >= 16 * 32 and matrix[:, -1].min() >= 8 * 32, matrix.min()
+        s = slice(1, STEPS_SHORT - 1)
+        step = np.median(pts[:, 2:STEPS_SHORT, 0] - pts[:, 1:STEPS_SHORT - 1, 0])
+        soft = np.median(pts[:, s, 3] - pts[:, s, 2])
+        pro = np.median(pts[:, 0, 0] - cal[:, 0])
+        epi = np.median(cal[:, 2] - pts[:, -1, 1])
+        life = np.median(cal[:, 2] - cal[:, 0])
+        print(f"[trace] workgroup {wg}: {mhz:.0f} MHz; prologue {pro:.0f}; step {step:.0f} "
+              f"(matrix {np.median(matrix[:, s]):.0f}, softmax + copies {soft:.0f}); write-back "
+              f"{epi:.0f}; wave life {life:.0f} = {life / mhz:.1f} us ({STEPS_SHORT} tiles)",
+              flush=True)
