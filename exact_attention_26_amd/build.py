@@ -16,6 +16,7 @@ them:
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -65,6 +66,40 @@ def compile_flags() -> list[str]:
     ]
 
 
+def source_stamp(extra: list[str] | None = None) -> str:
+    """Hash of everything a library build reads: the compiler flags (with the
+    variant's extra ones), the per-source flags, and the bytes of every
+    source and header under csrc/ and include/."""
+    h = hashlib.sha256()
+    # Paths are left out: the same tree may sit at another absolute path.
+    flags = [{INCLUDE: "<include>", CSRC: "<csrc>"}.get(f, f) for f in compile_flags()]
+    h.update(repr((flags, extra or [], sorted(EXTRA_FLAGS.items()), SOURCES)).encode())
+    for d in (CSRC, INCLUDE):
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".hip", ".h", ".cpp")):
+                h.update(name.encode())
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()
+
+
+def stamp_path(lib: str) -> str:
+    """The file next to a built library that holds its source_stamp()."""
+    return lib + ".stamp"
+
+
+def is_current(lib: str = LIB) -> bool:
+    """Whether the library variant at `lib` exists and was built from the
+    sources and flags now in the tree (its stamp matches)."""
+    extra = {path: ex for path, ex, _ in VARIANTS}.get(lib)
+    try:
+        with open(stamp_path(lib)) as f:
+            recorded = f.read().strip()
+    except OSError:
+        return False
+    return os.path.exists(lib) and extra is not None and recorded == source_stamp(extra)
+
+
 def build(verbose: bool = False) -> str:
     """Compile all sources of every variant (in parallel) and link them.
     Returns the path of the product library, libfa.so."""
@@ -96,13 +131,18 @@ def build(verbose: bool = False) -> str:
             failed.append(src)
     if failed:
         raise RuntimeError(f"hipcc failed for {failed}")
-    for lib, objs in links:
+    for (lib, objs), (_, extra, _) in zip(links, VARIANTS):
         tmp = lib + ".tmp"
         cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True)
         os.replace(tmp, lib)
+        # The stamp names the sources this library was built from, so that a
+        # stale library (sources edited since) can be told apart from a
+        # current one without rebuilding.
+        with open(stamp_path(lib), "w") as f:
+            f.write(source_stamp(extra) + "\n")
     return LIB
 
 

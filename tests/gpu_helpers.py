@@ -1,12 +1,14 @@
 """Shared helpers of the GPU tests (not a test module)."""
 from __future__ import annotations
 
+import os
 import sys
 
 import numpy as np
 import torch
 
 import exact_attention_26_amd as fa
+from exact_attention_26_amd import build as fa_build
 
 # Acceptance bounds on max |GPU - oracle|, per storage dtype: (O, L).
 TOL = {"fp32": (2e-5, 1e-5), "bf16": (2e-2, 5e-3), "fp16": (2e-2, 5e-3)}
@@ -16,6 +18,13 @@ def device() -> torch.device:
     if not torch.cuda.is_available():
         raise RuntimeError("GPU test run without a GPU")
     fa.load()  # fail loudly if the HIP library is missing
+    # ... or was built from other sources than those in the tree (the tests
+    # would then check old kernels).
+    stale = [os.path.basename(p) for p in (fa.LIB_PATH, fa.POISON_LIB_PATH, fa.TRACE_LIB_PATH)
+             if not fa_build.is_current(p)]
+    if stale:
+        raise RuntimeError(f"{', '.join(stale)} not built from the current sources; "
+                           "run python -m exact_attention_26_amd.build")
     return torch.device("cuda:0")
 
 
