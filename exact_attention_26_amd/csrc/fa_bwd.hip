@@ -407,6 +407,14 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2))) 
   const int qrc = min(qr, n - 1);
   const float lq = p.lse[(int64_t)bh * n + qrc] * 1.4426950408889634f;
   const float dq_nd = p.delta[(int64_t)bh * n + qrc];  // -D of this query
+  // d = 64: the dP^T chains start from -D (every accumulator value of a lane
+  // belongs to its query), held in 16 registers for the whole kernel, so the
+  // MFMAs produce dP - D and dS needs no add per element. At d = 128 the
+  // kernel has no 16 registers to spare (2 waves per SIMD) and adds -D.
+  constexpr bool ND_INIT = D == 64;
+  f32x16 nd16;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) nd16[i] = dq_nd;
   f32x16 acc[D / 32];  // dQ^T: d = 32t + 8(i/4) + 4g + i%4, query l32
 #pragma unroll
   for (int t = 0; t < D / 32; ++t)
@@ -452,7 +460,7 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2))) 
         const vec8 ka = *(const __attribute__((address_space(3))) vec8*)(Ks + T::off(r, cb));
         const vec8 va = *(const __attribute__((address_space(3))) vec8*)(Vs + T::off(r, cb));
         s[kt] = mfma32x32x16<BF16>(ka, qf[ss], s[kt]);
-        dp[kt] = mfma32x32x16<BF16>(va, of[ss], dp[kt]);
+        dp[kt] = mfma32x32x16<BF16>(va, of[ss], (ND_INIT && ss == 0) ? nd16 : dp[kt]);
       }
     // P^T then dS^T, one 32-key half at a time: the half's exponent arguments,
     // its exponentials, then its dS, as three fenced groups, so no instruction
@@ -481,7 +489,7 @@ __global__ __launch_bounds__(kThreadsB) __attribute__((amdgpu_waves_per_eu(2))) 
               const int key = k0 + kt * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
               if (key >= n) pv = 0.f;
             }
-            x[e] = pv * (dp[kt][i] + dq_nd);
+            x[e] = ND_INIT ? pv * dp[kt][i] : pv * (dp[kt][i] + dq_nd);
           }
           w[q] = pack2<BF16>(x[0], x[1]);
         }
